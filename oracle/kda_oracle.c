@@ -1,0 +1,232 @@
+/*
+ * kda_oracle.c -- plain double-precision CPU evaluation of one Kimi Delta
+ * Attention (KDA) decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker the GPU library is
+ * compared against.  It is called from the test suite, from the package's
+ * smoke check and from the CPU-baseline leg of the benchmark, and from
+ * nothing else.  It shares no code, header or constant with the HIP library.
+ *
+ * Every loop below is the definition written out, in the order and notation
+ * of the sources it cites; nothing is blocked, fused or reordered.  All
+ * arithmetic is IEEE double.  Inputs are BF16/FP32 values widened exactly to
+ * double by the caller.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [DD]  "GLM-5.3 deep dive" (gangliao.me, 2026):
+ *        8.2.2 (delta rule), 8.2.3 (KDA update, Eq. 1, and the order of
+ *        operations in fla's reference recurrence), 8.2.4 (the full layer:
+ *        short convolution with SiLU, split into heads, L2 normalisation),
+ *        8.2.6 (decoding: fade, predict, correct, read; epsilon 1e-6, q scale).
+ *  [P1]  "At the 262k cap the DSA indexer costs 12x the sparse MLA it selects
+ *        for", sections "Geometry" and "Bytes per stream" (depthwise conv,
+ *        kernel 4, 3 cached taps, 3 tensors).
+ *
+ * Readings taken where the pages leave a step open (each is listed with its
+ * reason in the design notes of the repository):
+ *  - conv: cross-correlation with causal left padding, no bias; tap 3
+ *    multiplies the current token, tap 0 the oldest cached token; the cached
+ *    taps are raw pre-conv inputs;
+ *  - L2 norm: x * 1/sqrt(sum x^2 + eps);
+ *  - the q scale is an argument (1/sqrt(D) in fla's decode, 1 in Eq. 1).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int kda_oracle_version(void) { return 1; }
+
+int kda_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Short causal convolution (kernel 4) followed by SiLU, for one stream of C
+ * independent channels.  [DD] 8.2.4 step 2; [P1] "Geometry".
+ *
+ *   y[c]  = w[c][0]*cs[0][c] + w[c][1]*cs[1][c] + w[c][2]*cs[2][c] + w[c][3]*x[c]
+ *   z[c]  = SiLU(y[c]) = y[c] / (1 + exp(-y[c]))
+ *   cs'   = (cs[1], cs[2], x)        (the three most recent raw inputs)
+ *
+ * Layouts: x[C], w[C][4], cs_in/cs_out[3][C] (tap 0 oldest), z[C].
+ * cs_out may equal cs_in.
+ */
+void kda_oracle_conv_silu(int C, const double *x, const double *w,
+                          const double *cs_in, double *cs_out, double *z)
+{
+    for (int c = 0; c < C; ++c) {
+        double t0 = cs_in[0 * (size_t)C + c];
+        double t1 = cs_in[1 * (size_t)C + c];
+        double t2 = cs_in[2 * (size_t)C + c];
+        double xc = x[c];
+        double y = w[4 * (size_t)c + 0] * t0 + w[4 * (size_t)c + 1] * t1 +
+                   w[4 * (size_t)c + 2] * t2 + w[4 * (size_t)c + 3] * xc;
+        z[c] = y / (1.0 + exp(-y));
+        cs_out[0 * (size_t)C + c] = t1;
+        cs_out[1 * (size_t)C + c] = t2;
+        cs_out[2 * (size_t)C + c] = xc;
+    }
+}
+
+/*
+ * L2 normalisation with epsilon, times a scale.  [DD] 8.2.4 step 6 and
+ * 8.2.6 implementation notes (epsilon 1e-6; q is then scaled).
+ *
+ *   out = scale * x / sqrt(sum_i x_i^2 + eps)
+ */
+void kda_oracle_l2norm(int n, const double *x, double eps, double scale,
+                       double *out)
+{
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i)
+        ss += x[i] * x[i];
+    double r = 1.0 / sqrt(ss + eps);
+    for (int i = 0; i < n; ++i)
+        out[i] = scale * x[i] * r;
+}
+
+/*
+ * One gated delta-rule step for one head.  [DD] 8.2.3 Eq. 1,
+ *
+ *   S_t = (I - beta k k^T) Diag(alpha) S_{t-1} + beta k v^T,   o = S_t^T q,
+ *
+ * evaluated in the decode order of [DD] 8.2.6 (fade, predict, correct, read),
+ * which 8.2.3 states is the same update as Eq. 1.
+ *
+ * S is [dk][dv], row i = key channel (the one alpha fades), column j = value
+ * channel.  q and k are used as given (already normalised and scaled).
+ * S is updated in place; o[dv] is written.
+ */
+void kda_oracle_delta_step(int dk, int dv, double *S, const double *q,
+                           const double *k, const double *v,
+                           const double *alpha, double beta, double *o)
+{
+    /* 1. fade: row i of S times alpha_i */
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] *= alpha[i];
+
+    /* 2. predict: vhat = S^T k with the faded state;
+     * 3. correct: S += k (beta (v - vhat))^T */
+    double *d = (double *)malloc(sizeof(double) * (size_t)(dv > 0 ? dv : 1));
+    for (int j = 0; j < dv; ++j) {
+        double vhat = 0.0;
+        for (int i = 0; i < dk; ++i)
+            vhat += S[(size_t)i * dv + j] * k[i];
+        d[j] = beta * (v[j] - vhat);
+    }
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] += k[i] * d[j];
+    free(d);
+
+    /* 4. read: o = S^T q with the new state */
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i)
+            acc += S[(size_t)i * dv + j] * q[i];
+        o[j] = acc;
+    }
+}
+
+/*
+ * One full KDA decode step over M streams and H heads of width D.
+ * [DD] 8.2.4 steps 2, 3 and 6, with 8.2.6's per-token order.
+ *
+ *   x      [M][3][H*D]     pre-conv q|k|v of this token
+ *   w      [3*H*D][4]      depthwise conv weights (q, k, v channels in order)
+ *   cs_in  [M][3][3*H*D]   conv state, tap 0 oldest; cs_out same (may alias)
+ *   S      [M][H][D][D]    recurrent state, updated in place
+ *   alpha  [M][H][D]       per key-channel decay
+ *   beta   [M][H]          write strength
+ *   o      [M][H][D]       output
+ *
+ * For each stream: conv + SiLU over all 3*H*D channels; split into heads;
+ * k^ = l2norm(k), q^ = scale * l2norm(q); then the delta step per head.
+ * Streams and heads are independent; OpenMP runs them in parallel.
+ */
+int kda_oracle_decode_step(int M, int H, int D, double *S, const double *x,
+                           const double *w, const double *cs_in,
+                           double *cs_out, const double *alpha,
+                           const double *beta, double scale, double eps,
+                           double *o)
+{
+    if (M < 0 || H < 1 || D < 1)
+        return 1;
+    const size_t HD = (size_t)H * D;
+    const size_t C = 3 * HD;
+    double *z = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1) * C);
+    if (!z)
+        return 2;
+
+    int m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m)
+        kda_oracle_conv_silu((int)C, x + (size_t)m * C, w,
+                             cs_in + (size_t)m * 3 * C,
+                             cs_out + (size_t)m * 3 * C, z + (size_t)m * C);
+
+    long unit;
+    const long units = (long)M * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (unit = 0; unit < units; ++unit) {
+        int mm = (int)(unit / H), h = (int)(unit % H);
+        const double *zq = z + (size_t)mm * C + 0 * HD + (size_t)h * D;
+        const double *zk = z + (size_t)mm * C + 1 * HD + (size_t)h * D;
+        const double *zv = z + (size_t)mm * C + 2 * HD + (size_t)h * D;
+        double *qh = (double *)malloc(sizeof(double) * (size_t)D);
+        double *kh = (double *)malloc(sizeof(double) * (size_t)D);
+        kda_oracle_l2norm(D, zq, eps, scale, qh);
+        kda_oracle_l2norm(D, zk, eps, 1.0, kh);
+        size_t u = (size_t)mm * H + h;
+        kda_oracle_delta_step(D, D, S + u * (size_t)D * D, qh, kh, zv,
+                              alpha + u * (size_t)D, beta[u], o + u * (size_t)D);
+        free(qh);
+        free(kh);
+    }
+    free(z);
+    return 0;
+}
+
+/*
+ * The recurrent part alone, from post-conv (post-SiLU) q|k|v:
+ *   qkv [M][3][H*D]; the rest as kda_oracle_decode_step.
+ * [DD] 8.2.4 step 6 with 8.2.6's order.
+ */
+int kda_oracle_recurrent_step(int M, int H, int D, double *S,
+                              const double *qkv, const double *alpha,
+                              const double *beta, double scale, double eps,
+                              double *o)
+{
+    if (M < 0 || H < 1 || D < 1)
+        return 1;
+    const size_t HD = (size_t)H * D;
+    long unit;
+    const long units = (long)M * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (unit = 0; unit < units; ++unit) {
+        int mm = (int)(unit / H), h = (int)(unit % H);
+        const double *zq = qkv + (size_t)mm * 3 * HD + 0 * HD + (size_t)h * D;
+        const double *zk = qkv + (size_t)mm * 3 * HD + 1 * HD + (size_t)h * D;
+        const double *zv = qkv + (size_t)mm * 3 * HD + 2 * HD + (size_t)h * D;
+        double *qh = (double *)malloc(sizeof(double) * (size_t)D);
+        double *kh = (double *)malloc(sizeof(double) * (size_t)D);
+        kda_oracle_l2norm(D, zq, eps, scale, qh);
+        kda_oracle_l2norm(D, zk, eps, 1.0, kh);
+        size_t u = (size_t)mm * H + h;
+        kda_oracle_delta_step(D, D, S + u * (size_t)D * D, qh, kh, zv,
+                              alpha + u * (size_t)D, beta[u], o + u * (size_t)D);
+        free(qh);
+        free(kh);
+    }
+    return 0;
+}

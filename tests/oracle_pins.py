@@ -1,0 +1,405 @@
+"""Pins that tie the CPU oracle to the pages and to mathematics, not to itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises ``AssertionError`` when
+the oracle disagrees with something it must reproduce:
+
+* values the pages print (the delta-rule worked example);
+* an independent algorithm for the same quantity (the unrolled product form
+  and the chunkwise WY/UT form of the recurrence);
+* library routines for the special cases that reduce to them
+  (torch's depthwise conv1d, SiLU and normalize, in float64);
+* closed forms and invariants the pages state (exact recall, identity at
+  alpha = 1 and beta = 0, the Householder contraction).
+
+``test_oracle_pins.py`` runs them on the real oracle; ``test_oracle_mutants.py``
+plants mistakes in a copy of the oracle's C source and checks that every
+planted mistake makes at least one pin fail.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    den = max(float(np.max(np.abs(b))), 1e-300)
+    err = float(np.max(np.abs(a - b))) / den if a.size else 0.0
+    assert err <= rtol, f"{what}: relative error {err:.3e} > {rtol:.1e}"
+
+
+def _unit(rng, n):
+    k = rng.standard_normal(n)
+    return k / np.linalg.norm(k)
+
+
+# --------------------------------------------------------------------------
+# 1. The pages' worked example ("GLM-5.3 deep dive", 8.2.2 step table)
+# --------------------------------------------------------------------------
+def _read_worked_example():
+    rows = []
+    with open(os.path.join(GOLDEN, "delta_rule_worked_example.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                tag, *vals = line.split()
+                rows.append((tag, [float(v) for v in vals]))
+    return rows
+
+
+def pin_worked_example(orc):
+    rows = _read_worked_example()
+    writes = [v for t, v in rows if t == "write"]
+    assert len(writes) == 3
+    one = np.ones(2)
+    S = np.zeros((2, 1))
+    states = {}
+    for step, k0, k1, val, s0, s1 in writes:
+        k = np.array([k0, k1])
+        S, _ = orc.delta_step(S, q=k, k=k, v=[val], alpha=one, beta=1.0)
+        _close(S[:, 0], [s0, s1], 1e-12, f"worked example S after step {int(step)}")
+        states[int(step)] = S.copy()
+    for t, vals in rows:
+        if t == "query_after":
+            step, q0, q1, expect = vals
+            Sq = states[int(step)]
+            # a read is o = S^T q; beta = 0 and alpha = 1 leave S as it is
+            _, o = orc.delta_step(Sq, q=[q0, q1], k=[1.0, 0.0], v=[0.0], alpha=one, beta=0.0)
+            _close(o, [expect], 1e-12, f"worked example query after step {int(step)}")
+        if t == "half_beta_step":
+            step, beta, expect = vals
+            k0, k1, val = writes[int(step) - 1][1:4]
+            S_prev = states[int(step) - 1]
+            S_half, _ = orc.delta_step(S_prev, q=[k0, k1], k=[k0, k1], v=[val],
+                                       alpha=one, beta=beta)
+            _close(S_half[0, 0], expect, 1e-12, "worked example with beta = 0.5")
+
+
+# --------------------------------------------------------------------------
+# 2. Brute force: the unrolled product form with explicit matrices
+#    S_T = A_T..A_1 S_0 + sum_t A_T..A_{t+1} beta_t k_t v_t^T,
+#    A_t = (I - beta_t k_t k_t^T) Diag(alpha_t)      ("GLM-5.3 deep dive" Eq. 1)
+# --------------------------------------------------------------------------
+def _unrolled(S0, ks, vs, alphas, betas, T):
+    dk = S0.shape[0]
+    A = [(np.eye(dk) - b * np.outer(k, k)) @ np.diag(a) for k, a, b in zip(ks, alphas, betas)]
+    P = np.eye(dk)
+    for t in range(T):
+        P = A[t] @ P
+    S = P @ S0
+    for t in range(T):
+        P = np.eye(dk)
+        for r in range(t + 1, T):
+            P = A[r] @ P
+        S = S + P @ (betas[t] * np.outer(ks[t], vs[t]))
+    return S
+
+
+def pin_unrolled_product(orc, dk=5, dv=3, T=6, seed=11):
+    rng = np.random.default_rng(seed)
+    S0 = rng.standard_normal((dk, dv))
+    ks = [_unit(rng, dk) for _ in range(T)]
+    qs = [rng.standard_normal(dk) for _ in range(T)]
+    vs = [rng.standard_normal(dv) for _ in range(T)]
+    alphas = [rng.uniform(0.2, 1.0, dk) for _ in range(T)]
+    betas = [float(rng.uniform(0.0, 1.0)) for _ in range(T)]
+    S = S0.copy()
+    for t in range(T):
+        S, o = orc.delta_step(S, qs[t], ks[t], vs[t], alphas[t], betas[t])
+        ref = _unrolled(S0, ks, vs, alphas, betas, t + 1)
+        _close(S, ref, 1e-12, f"unrolled form, state after step {t + 1}")
+        _close(o, ref.T @ qs[t], 1e-12, f"unrolled form, output at step {t + 1}")
+
+
+# --------------------------------------------------------------------------
+# 3. Independent algorithm: the chunkwise WY representation + UT transform
+#    ("GLM-5.3 deep dive" 8.2.5, Eq. 6-9).  Gamma_r is the inclusive
+#    cumulative decay; gamma^{i->C} excludes token i; StrictTril inside the
+#    inverse; Tril (with the diagonal) for the output.
+# --------------------------------------------------------------------------
+def _chunk_wy(S, K, Q, V, Alpha, beta):
+    C = K.shape[0]
+    G = np.cumprod(Alpha, axis=0)                   # Gamma [C, dk]
+    GK, KG, GQ = G * K, K / G, G * Q
+    Mx = np.linalg.inv(np.eye(C) + np.tril(np.diag(beta) @ GK @ KG.T, -1)) @ np.diag(beta)
+    W, U = Mx @ GK, Mx @ V
+    Delta = U - W @ S
+    O = GQ @ S + np.tril(GQ @ KG.T) @ Delta
+    S_next = np.diag(G[-1]) @ S + ((G[-1] / G) * K).T @ Delta
+    return S_next, O
+
+
+def pin_chunk_form(orc, dk=16, dv=16, C=16, seed=12):
+    rng = np.random.default_rng(seed)
+    S0 = rng.standard_normal((dk, dv)) * 0.1
+    K = np.stack([_unit(rng, dk) for _ in range(C)])
+    Q = rng.standard_normal((C, dk))
+    V = rng.standard_normal((C, dv))
+    Alpha = rng.uniform(0.5, 1.0, (C, dk))
+    beta = rng.uniform(0.0, 1.0, C)
+    S_ref, O_ref = _chunk_wy(S0, K, Q, V, Alpha, beta)
+    S = S0.copy()
+    O = np.empty((C, dv))
+    for t in range(C):
+        S, O[t] = orc.delta_step(S, Q[t], K[t], V[t], Alpha[t], beta[t])
+    _close(S, S_ref, 1e-11, "chunk WY form, final state")
+    _close(O, O_ref, 1e-11, "chunk WY form, outputs")
+
+
+# --------------------------------------------------------------------------
+# 4. Invariants stated by the pages
+# --------------------------------------------------------------------------
+def pin_identity_alpha1_beta0(orc, seed=13):
+    rng = np.random.default_rng(seed)
+    S0 = rng.standard_normal((8, 6))
+    q = rng.standard_normal(8)
+    S, o = orc.delta_step(S0, q, _unit(rng, 8), rng.standard_normal(6), np.ones(8), 0.0)
+    assert np.array_equal(S, S0), "alpha = 1, beta = 0 must leave S unchanged bit for bit"
+    _close(o, S0.T @ q, 1e-14, "alpha = 1, beta = 0 readout")
+
+
+def pin_pure_decay_beta0(orc, seed=14):
+    rng = np.random.default_rng(seed)
+    S0 = rng.standard_normal((8, 6))
+    a = rng.uniform(0, 1, 8)
+    S, _ = orc.delta_step(S0, np.zeros(8), _unit(rng, 8), rng.standard_normal(6), a, 0.0)
+    assert np.array_equal(S, S0 * a[:, None]), "beta = 0 must be a pure row decay"
+
+
+def pin_exact_recall(orc, seed=15):
+    """beta = 1 and a unit key: querying with that key returns v, whatever the
+    fade did ("GLM-5.3 deep dive" 8.2.3)."""
+    rng = np.random.default_rng(seed)
+    for dk, dv in ((2, 1), (7, 5), (16, 16)):
+        S0 = rng.standard_normal((dk, dv))
+        k = _unit(rng, dk)
+        v = rng.standard_normal(dv)
+        S, o = orc.delta_step(S0, k, k, v, rng.uniform(0, 1, dk), 1.0)
+        _close(o, v, 1e-13, f"exact recall dk={dk}")
+        _close(S.T @ k, v, 1e-13, f"exact recall via S^T k, dk={dk}")
+
+
+def pin_exact_recall_rational(orc):
+    """A Pythagorean unit key (3, 4, 12)/13 with rational alpha and state: the
+    recall with beta = 1 is exactly v, and the corrected state is known
+    exactly in rationals; the double oracle must agree to rounding."""
+    k = [Fraction(3, 13), Fraction(4, 13), Fraction(12, 13)]
+    S0 = [[Fraction(1, 2), Fraction(-1, 4)], [Fraction(3, 8), Fraction(1)], [Fraction(-2), Fraction(1, 16)]]
+    v = [Fraction(5, 4), Fraction(-3, 2)]
+    alpha = [Fraction(1, 2), Fraction(3, 4), Fraction(7, 8)]
+    # exact: faded state, prediction, corrected state, recall with beta = 1
+    Sf = [[alpha[i] * S0[i][j] for j in range(2)] for i in range(3)]
+    S_exact = [[Sf[i][j] + k[i] * (v[j] - sum(Sf[r][j] * k[r] for r in range(3)))
+                for j in range(2)] for i in range(3)]
+    S, o = orc.delta_step(np.array(S0, float), [float(x) for x in k], [float(x) for x in k],
+                          [float(x) for x in v], [float(x) for x in alpha], 1.0)
+    _close(o, [float(x) for x in v], 1e-14, "rational exact recall")
+    _close(S, np.array(S_exact, float), 1e-14, "rational corrected state")
+
+
+def pin_contraction(orc, seed=16):
+    """With |k| = 1 and beta in [0,1], I - beta k k^T has eigenvalue 1 - beta
+    along k and 1 elsewhere, so |S' - beta k v^T|_F <= |Diag(alpha) S|_F."""
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        dk, dv = 6, 4
+        S0 = rng.standard_normal((dk, dv))
+        k = _unit(rng, dk)
+        v = rng.standard_normal(dv)
+        a = rng.uniform(0, 1, dk)
+        b = float(rng.uniform(0, 1))
+        S, _ = orc.delta_step(S0, np.zeros(dk), k, v, a, b)
+        lhs = np.linalg.norm(S - b * np.outer(k, v))
+        rhs = np.linalg.norm(a[:, None] * S0)
+        assert lhs <= rhs * (1 + 1e-12), f"contraction violated: {lhs} > {rhs}"
+
+
+def pin_column_permutation(orc, seed=17):
+    """Value columns are independent: permuting them permutes S and o."""
+    rng = np.random.default_rng(seed)
+    dk, dv = 6, 5
+    S0 = rng.standard_normal((dk, dv))
+    q, k, v = rng.standard_normal(dk), _unit(rng, dk), rng.standard_normal(dv)
+    a = rng.uniform(0, 1, dk)
+    perm = rng.permutation(dv)
+    S1, o1 = orc.delta_step(S0, q, k, v, a, 0.7)
+    S2, o2 = orc.delta_step(S0[:, perm], q, k, v[perm], a, 0.7)
+    _close(S2, S1[:, perm], 1e-14, "column permutation, state")
+    _close(o2, o1[perm], 1e-14, "column permutation, output")
+
+
+# --------------------------------------------------------------------------
+# 5. Convolution and SiLU against torch's depthwise conv1d and silu (float64)
+#    ("GLM-5.3 deep dive" 8.2.4 step 2; "At the 262k cap ...", "Geometry")
+# --------------------------------------------------------------------------
+def pin_conv_library(orc, C=12, T=7, seed=18):
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((C, 4))
+    cs0 = rng.standard_normal((3, C))
+    xs = rng.standard_normal((T, C))
+    # torch: the three cached taps stand in for the causal left padding
+    seq = torch.from_numpy(np.concatenate([cs0, xs], 0).T[None])           # [1, C, 3+T]
+    y = F.conv1d(seq, torch.from_numpy(w)[:, None, :], groups=C)[0].T       # [T, C]
+    z_ref = F.silu(y).numpy()
+    cs = cs0
+    for t in range(T):
+        z, cs_next = orc.conv_silu(xs[t], w, cs)
+        _close(z, z_ref[t], 1e-13, f"conv+SiLU vs torch conv1d, token {t}")
+        assert np.array_equal(cs_next, np.concatenate([cs0, xs], 0)[t + 1:t + 4]), \
+            "conv state must hold the last three raw inputs, oldest first"
+        cs = cs_next
+
+
+def pin_conv_closed_forms(orc, C=8, seed=19):
+    rng = np.random.default_rng(seed)
+    # one-hot on the current tap: y = x
+    w = np.zeros((C, 4))
+    w[:, 3] = 1.0
+    x = rng.standard_normal(C)
+    z, _ = orc.conv_silu(x, w, rng.standard_normal((3, C)))
+    _close(z, F.silu(torch.from_numpy(x)).numpy(), 1e-15, "one-hot current tap")
+    # impulse response: tap 3 - t is what a unit impulse t tokens ago sees
+    w = rng.standard_normal((C, 4))
+    cs = np.zeros((3, C))
+    for t in range(4):
+        xt = np.ones(C) if t == 0 else np.zeros(C)
+        z, cs = orc.conv_silu(xt, w, cs)
+        _close(z, F.silu(torch.from_numpy(w[:, 3 - t].copy())).numpy(), 1e-15,
+               f"impulse response, {t} tokens after")
+    # SiLU closed values: SiLU(0) = 0 and SiLU(y) - SiLU(-y) = y
+    w = np.zeros((C, 4))
+    w[:, 3] = 1.0
+    y = np.linspace(-6, 6, C)
+    zp, _ = orc.conv_silu(y, w, np.zeros((3, C)))
+    zn, _ = orc.conv_silu(-y, w, np.zeros((3, C)))
+    _close(zp - zn, y, 1e-15, "SiLU odd part")
+    z0, _ = orc.conv_silu(np.zeros(C), w, np.zeros((3, C)))
+    assert np.all(z0 == 0.0)
+
+
+# --------------------------------------------------------------------------
+# 6. L2 norm ("GLM-5.3 deep dive" 8.2.6, epsilon 1e-6)
+# --------------------------------------------------------------------------
+def pin_l2norm(orc, seed=20):
+    _close(orc.l2norm([3.0, 4.0], eps=0.0), [0.6, 0.8], 1e-15, "l2norm (3,4)")
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(128)
+    ref = F.normalize(torch.from_numpy(x), dim=0, eps=0.0).numpy()
+    _close(orc.l2norm(x, eps=0.0), ref, 1e-15, "l2norm vs torch normalize")
+    _close(orc.l2norm(x, eps=0.0, scale=0.25), 0.25 * ref, 1e-15, "l2norm scale")
+    # epsilon: (1e-4, 0) -> 1e-4 / sqrt(1e-8 + 1e-6)
+    _close(orc.l2norm([1e-4, 0.0], eps=1e-6), [1e-4 / math.sqrt(1.01e-6), 0.0], 1e-15,
+           "l2norm epsilon")
+    assert np.all(orc.l2norm(np.zeros(5), eps=1e-6) == 0.0)
+
+
+# --------------------------------------------------------------------------
+# 7. End to end on tiny inputs: the fused step against a composition of
+#    torch conv1d + silu + normalize (eps = 0 on both sides) and the unrolled
+#    product form, over several tokens, streams and heads.
+# --------------------------------------------------------------------------
+def pin_decode_step_end_to_end(orc, M=2, H=3, D=4, T=5, seed=21):
+    rng = np.random.default_rng(seed)
+    HD, C = H * D, 3 * H * D
+    S0 = rng.standard_normal((M, H, D, D)) * 0.1
+    w = rng.standard_normal((C, 4)) * 0.5
+    cs0 = rng.standard_normal((M, 3, C))
+    xs = rng.standard_normal((T, M, 3, HD))
+    alphas = rng.uniform(0.3, 1.0, (T, M, H, D))
+    betas = rng.uniform(0.0, 1.0, (T, M, H))
+    scale = 1.0 / math.sqrt(D)
+
+    S, cs = S0.copy(), cs0.copy()
+    outs = []
+    for t in range(T):
+        S, cs, o = orc.decode_step(S, xs[t], w, cs, alphas[t], betas[t], scale, eps=0.0)
+        outs.append(o)
+
+    for m in range(M):
+        seq = np.concatenate([cs0[m], xs[:, m].reshape(T, C)], 0)            # [3+T, C]
+        y = F.conv1d(torch.from_numpy(seq.T[None]), torch.from_numpy(w)[:, None, :], groups=C)
+        z = F.silu(y)[0].T.numpy().reshape(T, 3, H, D)
+        for h in range(H):
+            q = F.normalize(torch.from_numpy(z[:, 0, h]), dim=1, eps=0.0).numpy() * scale
+            k = F.normalize(torch.from_numpy(z[:, 1, h]), dim=1, eps=0.0).numpy()
+            v = z[:, 2, h]
+            for t in range(T):
+                ref = _unrolled(S0[m, h], list(k), list(v), list(alphas[:, m, h]),
+                                list(betas[:, m, h]), t + 1)
+                _close(outs[t][m, h], ref.T @ q[t], 1e-12, f"end to end o, m={m} h={h} t={t}")
+            _close(S[m, h], ref, 1e-12, f"end to end state, m={m} h={h}")
+        assert np.array_equal(cs[m], seq[T:T + 3]), "end to end conv state"
+
+
+def pin_recurrent_matches_decode(orc, M=2, H=2, D=8, seed=22):
+    """The recurrent entry from post-conv q|k|v equals the fused step fed the
+    conv output, with the conv taken from torch."""
+    rng = np.random.default_rng(seed)
+    HD, C = H * D, 3 * H * D
+    S0 = rng.standard_normal((M, H, D, D))
+    w = rng.standard_normal((C, 4))
+    cs0 = rng.standard_normal((M, 3, C))
+    x = rng.standard_normal((M, 3, HD))
+    a = rng.uniform(0, 1, (M, H, D))
+    b = rng.uniform(0, 1, (M, H))
+    S1, _, o1 = orc.decode_step(S0, x, w, cs0, a, b, 0.5)
+    seq = np.concatenate([cs0, x.reshape(M, 1, C)], 1)                       # [M, 4, C]
+    y = F.conv1d(torch.from_numpy(seq.transpose(0, 2, 1).reshape(1, M * C, 4)),
+                 torch.from_numpy(np.tile(w, (M, 1)))[:, None, :], groups=M * C)
+    qkv = F.silu(y).numpy().reshape(M, 3, HD)
+    S2, o2 = orc.recurrent_step(S0, qkv, a, b, 0.5)
+    _close(S2, S1, 1e-14, "recurrent vs fused state")
+    _close(o2, o1, 1e-14, "recurrent vs fused output")
+
+
+def pin_unit_independence(orc, M=3, H=4, D=8, seed=23):
+    """Streams and heads are independent: changing one (stream, head)'s inputs
+    changes only that unit's state and output."""
+    rng = np.random.default_rng(seed)
+    HD, C = H * D, 3 * H * D
+    S0 = rng.standard_normal((M, H, D, D))
+    w = rng.standard_normal((C, 4))
+    cs0 = rng.standard_normal((M, 3, C))
+    x = rng.standard_normal((M, 3, HD))
+    a = rng.uniform(0, 1, (M, H, D))
+    b = rng.uniform(0, 1, (M, H))
+    S1, _, o1 = orc.decode_step(S0, x, w, cs0, a, b, 0.3)
+    m0, h0 = 1, 2
+    x2 = x.copy()
+    x2[m0, :, h0 * D:(h0 + 1) * D] += 1.0
+    a2 = a.copy()
+    a2[m0, h0] *= 0.5
+    S2, _, o2 = orc.decode_step(S0, x2, w, cs0, a2, b, 0.3)
+    for m in range(M):
+        for h in range(H):
+            same = (m, h) != (m0, h0)
+            assert np.array_equal(S1[m, h], S2[m, h]) == same, f"state unit ({m},{h})"
+            assert np.array_equal(o1[m, h], o2[m, h]) == same, f"output unit ({m},{h})"
+
+
+ALL_PINS = [
+    pin_worked_example,
+    pin_unrolled_product,
+    pin_chunk_form,
+    pin_identity_alpha1_beta0,
+    pin_pure_decay_beta0,
+    pin_exact_recall,
+    pin_exact_recall_rational,
+    pin_contraction,
+    pin_column_permutation,
+    pin_conv_library,
+    pin_conv_closed_forms,
+    pin_l2norm,
+    pin_decode_step_end_to_end,
+    pin_recurrent_matches_decode,
+    pin_unit_independence,
+]
