@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA decode step on one MI355X.
+
+One "step" is one token through all 34 KDA layers of GLM-5.3-Flash: 34
+launches of the fused decode kernel, each over M streams x 64 heads x
+128 x 128 state, every layer with its own state (so the state is read from
+HBM, not from the 256 MiB Infinity Cache).  Inputs are synthetic
+(``kda_synth``), resident in HBM before timing starts; 8 input sets (fresh
+q/k/v, alpha, beta per step) rotate across steps.
+
+Headline: M = 32 streams, FP32 state.  Also measured (``secondary``): M = 8
+with FP32 and BF16 state, M = 128 with BF16 state, and M = 1.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints ONE JSON line.  ``value`` is state GB/s = 2 * M * H * D^2 * bytes per
+layer (state read + written) over the measured time.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "decode_kernel_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "hybrid_linear_attention_kda_amd", "csrc", "kda_kernels.hip")
+METRIC = "KDA decode state GB/s + ms/layer at M=8,32 (FP32/BF16 state), % HBM peak"
+
+# algorithmic bytes per (stream, layer) besides the state: x 49,152 + conv
+# state read and written 294,912 + alpha 32,768 + beta 256 + o 16,384
+SIDE_BYTES_PER_STREAM = 393_472
+CONV_W_BYTES_PER_LAYER = 196_608
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Model:
+    """34 layers of device buffers plus pre-marshalled C-ABI arguments."""
+
+    def __init__(self, wl, state_dtype, n_inputs, device="cuda:0"):
+        import torch
+
+        import kda_synth
+        from hybrid_linear_attention_kda_amd import kda
+
+        self.wl, self.state_dtype = wl, state_dtype
+        self.lib = kda.load()
+        M, H, D = wl.M, wl.H, wl.D
+        self.layers = []
+        for layer in range(wl.layers):
+            li = kda_synth.layer_inputs(wl, layer, device, state_dtype)
+            o = torch.empty((M, H, D), dtype=torch.bfloat16, device=device)
+            ins = [kda_synth.step_inputs(wl, layer, t, device) for t in range(n_inputs)]
+            self.layers.append({"state": li["state"], "conv_w": li["conv_w"],
+                                "conv": li["conv_state"], "o": o, "inputs": ins})
+        torch.cuda.synchronize()
+        sdt = kda.KDA_STATE_F32 if state_dtype == "f32" else kda.KDA_STATE_BF16
+        self.n_inputs = n_inputs
+        self.args = []   # [input set][layer] -> tuple of C arguments (stream last)
+        vp = ctypes.c_void_p
+        for t in range(n_inputs):
+            row = []
+            for L in self.layers:
+                inp = L["inputs"][t]
+                row.append((M, H, D, sdt, vp(L["state"].data_ptr()), vp(inp["x"].data_ptr()),
+                            vp(L["conv_w"].data_ptr()), vp(L["conv"].data_ptr()),
+                            vp(L["conv"].data_ptr()), vp(inp["alpha"].data_ptr()),
+                            vp(inp["beta"].data_ptr()), ctypes.c_float(wl.scale),
+                            vp(L["o"].data_ptr())))
+            self.args.append(row)
+
+    def state_bytes_per_layer(self):
+        return self.wl.state_bytes(self.state_dtype)
+
+    def alg_bytes_per_launch(self):
+        return (self.state_bytes_per_layer() * 2 + self.wl.M * SIDE_BYTES_PER_STREAM
+                + CONV_W_BYTES_PER_LAYER)
+
+    def step(self, t, stream_ptr):
+        fn = self.lib.kda_decode_step
+        s = ctypes.c_void_p(stream_ptr)
+        for a in self.args[t % self.n_inputs]:
+            rc = fn(*a, s)
+            if rc:
+                raise RuntimeError(f"kda_decode_step returned {rc}")
+
+
+def time_model(model, steps, warmup, use_graph):
+    """Return (seconds for `steps` steps, mode)."""
+    import torch
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        sp = stream.cuda_stream
+        for w in range(warmup):
+            model.step(w, sp)
+        stream.synchronize()
+        graphs = None
+        if use_graph:
+            graphs = []
+            for t in range(model.n_inputs):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    model.step(t, torch.cuda.current_stream().cuda_stream)
+                graphs.append(g)
+            for g in graphs:           # one untimed replay of each
+                g.replay()
+            stream.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(steps):
+            if graphs is not None:
+                graphs[k % len(graphs)].replay()
+            else:
+                model.step(k, sp)
+        end.record(stream)
+        end.synchronize()
+        torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3, ("hipGraph" if use_graph else "eager")
+
+
+def measure(wl, state_dtype, steps, warmup, n_inputs):
+    model = Model(wl, state_dtype, n_inputs)
+    res = {}
+    for use_graph in (False, True):
+        sec, mode = time_model(model, steps, warmup, use_graph)
+        launches = steps * wl.layers
+        res[mode] = {
+            "ms_per_step": sec * 1e3 / steps,
+            "ms_per_layer": sec * 1e3 / launches,
+            "state_GBps": 2 * model.state_bytes_per_layer() * launches / sec / 1e9,
+            "alg_GBps": model.alg_bytes_per_launch() * launches / sec / 1e9,
+        }
+    best = max(res, key=lambda m: res[m]["state_GBps"])
+    out = dict(res[best])
+    out["launch"] = best
+    out["modes"] = res
+    out["alg_bytes_per_launch"] = model.alg_bytes_per_launch()
+    out["state_bytes_per_launch"] = 2 * model.state_bytes_per_layer()
+    del model
+    import torch
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_ceiling(gib=4.0):
+    """Plain device-to-device copy of `gib` GiB (1:1 read:write): the
+    achievable HBM ceiling for a stream that reads and writes equal bytes."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    e.synchronize()
+    sec = s.elapsed_time(e) / 1e3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / sec / 1e9
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The CPU oracle (double precision, OpenMP over (stream, head) units) on a
+    bounded sample of the same workload: consecutive layers, one step each,
+    until about `budget_s` seconds of CPU time are spent."""
+    import torch
+
+    import kda_synth
+    import oracle
+    orc = oracle.get()
+    done, elapsed = 0, 0.0
+    while elapsed < budget_s and done < wl.layers:
+        li = kda_synth.layer_inputs(wl, done, "cpu", "f32")
+        inp = kda_synth.step_inputs(wl, done, 0, "cpu")
+        h = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+        S, x, w, cs = h(li["state"]), h(inp["x"]), h(li["conv_w"]), h(li["conv_state"])
+        a, b = h(inp["alpha"]), h(inp["beta"])
+        t0 = time.perf_counter()
+        orc.decode_step(S, x, w, cs, a, b, wl.scale)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    state_bytes = 2 * wl.state_bytes("f32") * done
+    return {
+        "value": state_bytes / elapsed / 1e9,
+        "unit": "GB/s",
+        "cores": orc.max_threads(),
+        "kind": "oracle",
+        "sample": f"{done} of {wl.layers} layers x 1 step of the same workload "
+                  f"(M={wl.M}, 64x128x128, state bytes counted as FP32), "
+                  f"{elapsed:.1f} s, {elapsed / done * 1e3:.1f} ms/layer",
+    }
+
+
+def stored_traffic(alg_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    if the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the KDA decode step shards by stream with no "
+              f"communication, so --gpus {args.gpus} is not run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kda_synth
+    from hybrid_linear_attention_kda_amd import kda
+    kda.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    wl = kda_synth.WORKLOADS["glm_m32"]
+    log(f"headline: {wl.description}")
+    head = measure(wl, "f32", args.steps, args.warmup, n_inputs=wl.steps)
+    log(f"  {json.dumps({k: head[k] for k in ('launch', 'ms_per_step', 'ms_per_layer', 'state_GBps')})}")
+
+    secondary = []
+    if not args.no_secondary:
+        for name, sdt in (("glm_m8", "f32"), ("glm_m8", "bf16"), ("glm_m128", "bf16"),
+                          ("glm_m1", "f32")):
+            w2 = kda_synth.WORKLOADS[name]
+            if name == "glm_m1":
+                w2 = kda_synth.Workload(**{**w2.__dict__, "layers": 34, "name": "glm_m1_34"})
+            r = measure(w2, sdt, max(20, args.steps // 4), args.warmup, n_inputs=min(w2.steps, 8))
+            entry = {"workload": name, "M": w2.M, "layers": w2.layers, "state_dtype": sdt,
+                     "launch": r["launch"], "ms_per_layer": r["ms_per_layer"],
+                     "ms_per_34_layer_step": r["ms_per_step"], "state_GBps": r["state_GBps"],
+                     "frac_hbm_peak_state": r["state_GBps"] / HBM_PEAK_GBS,
+                     "modes": r["modes"]}
+            secondary.append(entry)
+            log(f"  {name} {sdt}: {r['launch']} {r['ms_per_layer'] * 1e3:.2f} us/layer "
+                f"{r['state_GBps']:.0f} GB/s")
+
+    copy_gbs = None if args.no_copy else copy_ceiling()
+    if copy_gbs:
+        log(f"  copy ceiling {copy_gbs:.0f} GB/s")
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+
+    avg_launch_s = head["ms_per_layer"] / 1e3
+    achieved = head["alg_bytes_per_launch"] / avg_launch_s / 1e9
+    roof = {
+        "bound": "hbm",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBS,
+        "traffic": stored_traffic(head["alg_bytes_per_launch"]),
+        "kernel": "decode_kernel<float, D=128, NSPLIT=1, NWAVES=4, VEC=4>",
+        "alg_bytes_per_launch": head["alg_bytes_per_launch"],
+        "avg_launch_us": avg_launch_s * 1e6,
+    }
+    out = {
+        "metric": METRIC,
+        "value": head["state_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "glm_m32: GLM-5.3-Flash KDA decode, M=32 streams, 34 layers with "
+                               "distinct states, 64 heads x 128 x 128, FP32 state (4.25 GiB), "
+                               "8 rotating input sets",
+                   "M": wl.M, "H": wl.H, "D": wl.D, "layers": wl.layers, "state_dtype": "f32",
+                   "launch": head["launch"]},
+        "ms_per_layer": head["ms_per_layer"],
+        "frac_hbm_peak_state": head["state_GBps"] / HBM_PEAK_GBS,
+        "modes": head["modes"],
+        "copy_ceiling_GBps": copy_gbs,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

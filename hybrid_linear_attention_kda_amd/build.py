@@ -1,0 +1,54 @@
+"""Build ``libkda.so`` (the gfx950 HIP library behind ``include/kda.h``).
+
+    python -m hybrid_linear_attention_kda_amd.build
+
+Compiles ``csrc/kda_kernels.hip`` and ``csrc/kda_api.cpp`` with hipcc for
+gfx950 only.  Packed-FP32 instructions are switched off for device code.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(PKG, "libkda.so")
+SOURCES = [os.path.join(CSRC, "kda_kernels.hip"), os.path.join(CSRC, "kda_api.cpp")]
+HEADERS = [os.path.join(INCLUDE, "kda.h"), os.path.join(CSRC, "kda_launch.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile the library to ``output``; returns its path."""
+    tmp = output + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(extra or []), f"-I{INCLUDE}", f"-I{CSRC}", *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode})")
+    os.replace(tmp, output)
+    return output
+
+
+def is_stale(path: str = LIBRARY) -> bool:
+    if not os.path.exists(path):
+        return True
+    t = os.path.getmtime(path)
+    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,220 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h.
+//
+// Host-side argument validation (before any HIP call), launch-shape choice,
+// and error mapping.  The library holds no state besides a per-device cache
+// of the compute-unit count.
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+inline Range span(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+
+// Size of M * a * b * c elements of `bytes` each; false on overflow or if the
+// element count exceeds what the kernels index with 32-bit unit counts.
+bool checked_bytes(long M, long a, long b, long c, long bytes, size_t* out) {
+    const long long lim = (1LL << 46);
+    long long n = (long long)M;
+    const long f[3] = {a, b, c};
+    for (long v : f) {
+        if (v < 0 || (v > 0 && n > lim / v)) return false;
+        n *= v;
+    }
+    if (n > lim / bytes) return false;
+    *out = (size_t)(n * bytes);
+    return true;
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// Workgroups per head.  A head is one workgroup (64 KiB of f32 state) unless
+// M*H is too small to fill the device, in which case its value columns are
+// split.  Splitting needs distinct conv buffers: the split workgroups of a head
+// all read the head's q/k taps, so none may overwrite them in place.
+int choose_split(int M, int H, int D, bool conv_in_place) {
+    if (D != 128 || conv_in_place) return 1;
+    const long units = (long)M * H;
+    int cus = kda::device_cu_count();
+    if (cus <= 0) cus = 256;
+    if (units >= 4L * cus) return 1;
+    if (units >= 2L * cus) return 2;
+    return 4;
+}
+
+struct StepSizes {
+    size_t state, x, w, conv, alpha, beta, o, qkv;
+};
+
+int step_sizes(int M, int H, int D, int sdt, StepSizes* s) {
+    const long HD = (long)H * D;
+    const long sb = sdt == KDA_STATE_F32 ? 4 : 2;
+    if (!checked_bytes(M, H, D, D, sb, &s->state)) return KDA_ERR_ARG;
+    if (!checked_bytes(M, 3, HD, 1, 2, &s->x)) return KDA_ERR_ARG;
+    if (!checked_bytes(1, 3, HD, 4, 2, &s->w)) return KDA_ERR_ARG;
+    if (!checked_bytes(M, 3, 3, HD, 2, &s->conv)) return KDA_ERR_ARG;
+    if (!checked_bytes(M, H, D, 1, 4, &s->alpha)) return KDA_ERR_ARG;
+    if (!checked_bytes(M, H, 1, 1, 4, &s->beta)) return KDA_ERR_ARG;
+    if (!checked_bytes(M, H, D, 1, 2, &s->o)) return KDA_ERR_ARG;
+    if (!checked_bytes(M, 3, HD, 1, 4, &s->qkv)) return KDA_ERR_ARG;
+    // the kernels index workgroups as M*H*nsplit in 32 bits
+    if ((long long)M * H * 4 > 0x7fffffffLL) return KDA_ERR_ARG;
+    return KDA_OK;
+}
+
+int check_common(int M, int H, int D, int sdt, float scale) {
+    if (M < 0) return KDA_ERR_ARG;
+    if (H < 1 || !supported_d(D)) return KDA_ERR_SHAPE;
+    if (sdt != KDA_STATE_F32 && sdt != KDA_STATE_BF16) return KDA_ERR_DTYPE;
+    if (!isfinite(scale)) return KDA_ERR_ARG;
+    return KDA_OK;
+}
+
+int validate_decode(int M, int H, int D, int sdt, void* state, const void* x, const void* w,
+                    const void* cin, void* cout, const float* alpha, const float* beta,
+                    float scale, void* o, StepSizes* sz) {
+    int rc = check_common(M, H, D, sdt, scale);
+    if (rc != KDA_OK) return rc;
+    if (M == 0) return KDA_OK;
+    if (!state || !x || !w || !cin || !cout || !alpha || !beta || !o) return KDA_ERR_NULL;
+    const void* ptrs[] = {state, x, w, cin, cout, alpha, beta, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    rc = step_sizes(M, H, D, sdt, sz);
+    if (rc != KDA_OK) return rc;
+    const Range rs = span(state, sz->state), ro = span(o, sz->o), rco = span(cout, sz->conv);
+    const Range inputs[] = {span(x, sz->x), span(w, sz->w), span(cin, sz->conv),
+                            span(alpha, sz->alpha), span(beta, sz->beta)};
+    for (const Range& r : inputs)
+        if (overlap(rs, r) || overlap(ro, r)) return KDA_ERR_ALIAS;
+    if (overlap(rs, ro) || overlap(rs, rco) || overlap(ro, rco)) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i) {
+        if (i == 2 && cout == cin) continue;  // exact in-place conv state is allowed
+        if (overlap(rco, inputs[i])) return KDA_ERR_ALIAS;
+    }
+    return KDA_OK;
+}
+
+int run_decode(int M, int H, int D, int sdt, void* state, const void* x, const void* w,
+               const void* cin, void* cout, const float* alpha, const float* beta,
+               float scale, void* o, void* stream, int nsplit) {
+    StepSizes sz;
+    int rc = validate_decode(M, H, D, sdt, state, x, w, cin, cout, alpha, beta, scale, o, &sz);
+    if (rc != KDA_OK || M == 0) return rc;
+    const bool in_place = cout == cin;
+    if (nsplit == 0) {
+        nsplit = choose_split(M, H, D, in_place);
+    } else {
+        if (nsplit != 1 && nsplit != 2 && nsplit != 4) return KDA_ERR_ARG;
+        if (nsplit > 1 && (D != 128 || in_place)) return KDA_ERR_ARG;
+    }
+    kda::StepArgs a{};
+    a.M = M; a.H = H; a.D = D; a.state_dtype = sdt; a.nsplit = nsplit;
+    a.state = state; a.x = x; a.conv_w = w; a.conv_in = cin; a.conv_out = cout;
+    a.qkv = nullptr; a.alpha = alpha; a.beta = beta; a.scale = scale; a.o = o;
+    a.stream = stream;
+    return map_hip(kda::launch_decode_step(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_decode_step(int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                    const void* conv_w, const void* conv_in, void* conv_out, const float* alpha,
+                    const float* beta, float scale, void* o, void* stream) {
+    return run_decode(M, H, D, state_dtype, state, x_qkv, conv_w, conv_in, conv_out, alpha, beta,
+                      scale, o, stream, 0);
+}
+
+int kda_decode_step_split(int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                          const void* conv_w, const void* conv_in, void* conv_out,
+                          const float* alpha, const float* beta, float scale, void* o,
+                          void* stream, int nsplit) {
+    if (nsplit < 1) return KDA_ERR_ARG;
+    return run_decode(M, H, D, state_dtype, state, x_qkv, conv_w, conv_in, conv_out, alpha, beta,
+                      scale, o, stream, nsplit);
+}
+
+int kda_conv_step(int M, int C, const void* x, const void* conv_w, const void* conv_in,
+                  void* conv_out, float* y, void* stream) {
+    if (M < 0 || C < 1 || (C % 8) != 0) return KDA_ERR_ARG;
+    if (M == 0) return KDA_OK;
+    if (!x || !conv_w || !conv_in || !conv_out || !y) return KDA_ERR_NULL;
+    const void* ptrs[] = {x, conv_w, conv_in, conv_out, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    size_t bx, bw, bc, by;
+    if (!checked_bytes(M, C, 1, 1, 2, &bx) || !checked_bytes(1, C, 4, 1, 2, &bw) ||
+        !checked_bytes(M, 3, C, 1, 2, &bc) || !checked_bytes(M, C, 1, 1, 4, &by))
+        return KDA_ERR_ARG;
+    if ((long long)M * (C / 8) > 0x7fffffffLL * 256LL) return KDA_ERR_ARG;
+    const Range ry = span(y, by), rco = span(conv_out, bc);
+    const Range rx = span(x, bx), rw = span(conv_w, bw), rci = span(conv_in, bc);
+    if (overlap(ry, rx) || overlap(ry, rw) || overlap(ry, rci) || overlap(ry, rco))
+        return KDA_ERR_ALIAS;
+    if (overlap(rco, rx) || overlap(rco, rw)) return KDA_ERR_ALIAS;
+    if (conv_out != conv_in && overlap(rco, rci)) return KDA_ERR_ALIAS;
+    return map_hip(kda::launch_conv_step(M, C, x, conv_w, conv_in, conv_out, y, stream));
+}
+
+int kda_recurrent_step(int M, int H, int D, int state_dtype, void* state, const float* qkv,
+                       const float* alpha, const float* beta, float scale, void* o,
+                       void* stream) {
+    int rc = check_common(M, H, D, state_dtype, scale);
+    if (rc != KDA_OK) return rc;
+    if (M == 0) return KDA_OK;
+    if (!state || !qkv || !alpha || !beta || !o) return KDA_ERR_NULL;
+    const void* ptrs[] = {state, qkv, alpha, beta, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    StepSizes sz;
+    rc = step_sizes(M, H, D, state_dtype, &sz);
+    if (rc != KDA_OK) return rc;
+    const Range rs = span(state, sz.state), ro = span(o, sz.o);
+    const Range inputs[] = {span(qkv, sz.qkv), span(alpha, sz.alpha), span(beta, sz.beta)};
+    for (const Range& r : inputs)
+        if (overlap(rs, r) || overlap(ro, r)) return KDA_ERR_ALIAS;
+    if (overlap(rs, ro)) return KDA_ERR_ALIAS;
+    kda::StepArgs a{};
+    a.M = M; a.H = H; a.D = D; a.state_dtype = state_dtype;
+    a.nsplit = choose_split(M, H, D, false);
+    a.state = state; a.qkv = qkv; a.alpha = alpha; a.beta = beta; a.scale = scale; a.o = o;
+    a.stream = stream;
+    return map_hip(kda::launch_recurrent_step(a));
+}
+
+const char* kda_status_string(int status) {
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "unsupported shape (H < 1 or D not in {16, 32, 64, 128})";
+    case KDA_ERR_DTYPE: return "unknown state dtype";
+    case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KDA_ERR_ALIAS: return "an output overlaps an input";
+    case KDA_ERR_ARG: return "invalid argument (negative size, non-finite scale, overflow)";
+    case KDA_ERR_HIP: return "the HIP runtime refused the launch";
+    default: return "unknown status";
+    }
+}
+
+int kda_version(void) { return 10000; }
+
+}  // extern "C"

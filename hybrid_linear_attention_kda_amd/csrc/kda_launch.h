@@ -1,0 +1,35 @@
+// kda_launch.h -- internal interface between the C ABI (kda_api.cpp) and the
+// gfx950 kernels (kda_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+// Arguments of one decode / recurrent launch, already validated by the host.
+struct StepArgs {
+    int M, H, D;
+    int state_dtype;      // 0 = f32, 1 = bf16
+    int nsplit;           // workgroups per head: 1, 2 or 4 (D == 128 only)
+    void* state;
+    const void* x;        // bf16 [M][3][H*D]        (fused step)
+    const void* conv_w;   // bf16 [3*H*D][4]         (fused step)
+    const void* conv_in;  // bf16 [M][3][3*H*D]      (fused step)
+    void* conv_out;       // bf16 [M][3][3*H*D]      (fused step)
+    const float* qkv;     // f32  [M][3][H*D]        (recurrent step)
+    const float* alpha;
+    const float* beta;
+    float scale;
+    void* o;
+    void* stream;
+};
+
+hipError_t launch_decode_step(const StepArgs& a);
+hipError_t launch_recurrent_step(const StepArgs& a);
+hipError_t launch_conv_step(int M, int C, const void* x, const void* w, const void* cin,
+                            void* cout, float* y, void* stream);
+
+// Compute units of the current device (0 if unknown).
+int device_cu_count();
+
+}  // namespace kda

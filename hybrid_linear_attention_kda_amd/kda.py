@@ -1,0 +1,182 @@
+"""Python binding of ``libkda.so`` (argument marshalling only).
+
+Each function has the name and argument order of its C entry point in
+``include/kda.h``.  Shapes, dtypes and devices are derived from torch
+tensors and checked here, because the C ABI receives bare pointers and
+cannot see buffer sizes; every step of the computation runs in the HIP
+kernels.  There is no fallback: if the library is not built, importing the
+binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+#: the built library (see ``build.py``)
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE = 0, 1, 2, 3
+KDA_ERR_ALIGN, KDA_ERR_ALIAS, KDA_ERR_ARG, KDA_ERR_HIP = 4, 5, 6, 7
+KDA_STATE_F32, KDA_STATE_BF16 = 0, 1
+
+#: every symbol ``include/kda.h`` declares
+EXPORTS = ("kda_decode_step", "kda_decode_step_split", "kda_conv_step",
+           "kda_recurrent_step", "kda_status_string", "kda_version")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+_LIB = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the HIP library (once) and declare its C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run `python -m hybrid_linear_attention_kda_amd.build`")
+    lib = ctypes.CDLL(path)
+    i, f, vp, fp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p
+    step = [i, i, i, i, vp, vp, vp, vp, vp, fp, fp, f, vp, vp]
+    lib.kda_decode_step.argtypes = step
+    lib.kda_decode_step.restype = i
+    lib.kda_decode_step_split.argtypes = step + [i]
+    lib.kda_decode_step_split.restype = i
+    lib.kda_conv_step.argtypes = [i, i, vp, vp, vp, vp, fp, vp]
+    lib.kda_conv_step.restype = i
+    lib.kda_recurrent_step.argtypes = [i, i, i, i, vp, fp, fp, fp, f, vp, vp]
+    lib.kda_recurrent_step.restype = i
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = i
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(int(status)).decode()
+
+
+def kda_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def kda_version() -> int:
+    return int(load().kda_version())
+
+
+# ------------------------------------------------------------ marshalling --
+def _need(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _p(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _state_code(state: torch.Tensor) -> int:
+    if state.dtype == torch.float32:
+        return KDA_STATE_F32
+    if state.dtype == torch.bfloat16:
+        return KDA_STATE_BF16
+    raise TypeError(f"state must be float32 or bfloat16, not {state.dtype}")
+
+
+def _check(fn, rc):
+    if rc != KDA_OK:
+        raise KdaError(fn, rc)
+
+
+def kda_decode_step(state, x_qkv, conv_w, conv_in, conv_out, alpha, beta, scale, o,
+                    stream=None, nsplit: int | None = None):
+    """Fused KDA decode step over M streams (see ``kda_decode_step`` in kda.h).
+
+    state [M,H,D,D] f32|bf16 (in place), x_qkv [M,3,H*D] bf16,
+    conv_w [3*H*D,4] bf16, conv_in/conv_out [M,3,3*H*D] bf16 (may be the same
+    tensor), alpha [M,H,D] f32, beta [M,H] f32, o [M,H,D] bf16.
+    ``nsplit`` forces the workgroups-per-head split (1, 2, 4).
+    """
+    lib = load()
+    if state.dim() != 4:
+        raise ValueError("state must be [M, H, D, D]")
+    M, H, D, _ = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("state must be a GPU tensor")
+    _need(state, "state", (M, H, D, D), state.dtype, dev)
+    _need(x_qkv, "x_qkv", (M, 3, H * D), torch.bfloat16, dev)
+    _need(conv_w, "conv_w", (3 * H * D, 4), torch.bfloat16, dev)
+    _need(conv_in, "conv_in", (M, 3, 3 * H * D), torch.bfloat16, dev)
+    _need(conv_out, "conv_out", (M, 3, 3 * H * D), torch.bfloat16, dev)
+    _need(alpha, "alpha", (M, H, D), torch.float32, dev)
+    _need(beta, "beta", (M, H), torch.float32, dev)
+    _need(o, "o", (M, H, D), torch.bfloat16, dev)
+    args = (M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w), _p(conv_in),
+            _p(conv_out), _p(alpha), _p(beta), float(scale), _p(o), _stream(dev, stream))
+    if nsplit is None:
+        _check("kda_decode_step", lib.kda_decode_step(*args))
+    else:
+        _check("kda_decode_step_split", lib.kda_decode_step_split(*args, int(nsplit)))
+
+
+def kda_conv_step(x, conv_w, conv_in, conv_out, y, stream=None):
+    """Conv + SiLU over C channels: x [M,C] bf16, conv_w [C,4] bf16,
+    conv_in/conv_out [M,3,C] bf16, y [M,C] f32."""
+    lib = load()
+    if x.dim() != 2:
+        raise ValueError("x must be [M, C]")
+    M, C = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    _need(x, "x", (M, C), torch.bfloat16, dev)
+    _need(conv_w, "conv_w", (C, 4), torch.bfloat16, dev)
+    _need(conv_in, "conv_in", (M, 3, C), torch.bfloat16, dev)
+    _need(conv_out, "conv_out", (M, 3, C), torch.bfloat16, dev)
+    _need(y, "y", (M, C), torch.float32, dev)
+    _check("kda_conv_step", lib.kda_conv_step(M, C, _p(x), _p(conv_w), _p(conv_in), _p(conv_out),
+                                              _p(y), _stream(dev, stream)))
+
+
+def kda_recurrent_step(state, qkv, alpha, beta, scale, o, stream=None):
+    """Recurrent part from post-conv q|k|v [M,3,H*D] f32; other args as kda_decode_step."""
+    lib = load()
+    if state.dim() != 4:
+        raise ValueError("state must be [M, H, D, D]")
+    M, H, D, _ = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("state must be a GPU tensor")
+    _need(state, "state", (M, H, D, D), state.dtype, dev)
+    _need(qkv, "qkv", (M, 3, H * D), torch.float32, dev)
+    _need(alpha, "alpha", (M, H, D), torch.float32, dev)
+    _need(beta, "beta", (M, H), torch.float32, dev)
+    _need(o, "o", (M, H, D), torch.bfloat16, dev)
+    _check("kda_recurrent_step",
+           lib.kda_recurrent_step(M, H, D, _state_code(state), _p(state), _p(qkv), _p(alpha),
+                                  _p(beta), float(scale), _p(o), _stream(dev, stream)))

@@ -1,0 +1,147 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention decode step.
+ *
+ * One call advances M independent streams of one KDA layer by one token:
+ *
+ *   1. short causal convolution (kernel 4, three cached taps) + SiLU over the
+ *      q, k and v channels ("GLM-5.3 deep dive", 8.2.4 step 2; "At the 262k
+ *      cap the DSA indexer costs 12x the sparse MLA it selects for",
+ *      "Geometry": depthwise, kernel 4, 3 taps, 3 tensors);
+ *   2. per-head L2 normalisation of q and k, and the q scale (8.2.4 step 6;
+ *      8.2.6 implementation notes: epsilon 1e-6, q scaled after the norm);
+ *   3. the gated delta rule on the per-head [D x D] state and the readout
+ *      (8.2.3 Eq. 1:  S' = (I - b k k^T) Diag(a) S + b k v^T,  o = S'^T q,
+ *      evaluated as fade, predict, correct, read: 8.2.6).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers to memory the caller owns.  The
+ *   library never allocates, frees, synchronises, or keeps state between
+ *   calls.  Every pointer must be 16-byte aligned.
+ * - Arrays are dense, row-major, last index fastest.  "bf16" is the 16-bit
+ *   bfloat16 bit pattern (uint16); "f32" is IEEE binary32.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *   and runs asynchronously.  KDA_OK means the work was enqueued; faults
+ *   during execution surface at the caller's next synchronisation.
+ * - Every argument check happens on the host before any HIP call, so an
+ *   invalid call returns its status without touching the GPU.
+ * - M == 0 is an empty batch: KDA_OK, nothing is read or written.
+ * - Results are bitwise deterministic for a given input, shape and device.
+ * - Values outside the stated ranges (alpha, beta not in [0, 1], NaN) are the
+ *   caller's contract and are not checked on the device.
+ * - Rounding to bf16 is round-to-nearest-even; all arithmetic is f32.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,   /* a required pointer is NULL                         */
+    KDA_ERR_SHAPE = 2,  /* H < 1, or D not one of the supported head widths   */
+    KDA_ERR_DTYPE = 3,  /* state_dtype is not a kda_state_dtype               */
+    KDA_ERR_ALIGN = 4,  /* a pointer is not 16-byte aligned                   */
+    KDA_ERR_ALIAS = 5,  /* an output overlaps an input it may not overlap     */
+    KDA_ERR_ARG = 6,    /* M < 0, C < 1, non-finite scale, sizes overflow     */
+    KDA_ERR_HIP = 7     /* the HIP runtime refused the launch                 */
+};
+
+/* Storage type of the recurrent state.  Arithmetic is f32 either way. */
+typedef enum { KDA_STATE_F32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype;
+
+/* epsilon inside the L2 norm: x * 1/sqrt(sum x^2 + eps) */
+#define KDA_L2NORM_EPS 1e-6f
+
+/* Supported head widths D (= dk = dv): 16, 32, 64, 128. */
+
+/*
+ * kda_decode_step -- the fused step: conv + SiLU, L2 norm, gated delta
+ * update and readout, for M streams x H heads of width D.
+ *
+ *  state   [M][H][D][D]  f32 or bf16 (state_dtype), updated in place.
+ *                        Row i is key channel i (faded by alpha_i), column j
+ *                        is value channel j.
+ *  x_qkv   [M][3][H*D]   bf16: this token's pre-conv q, k, v (projections).
+ *  conv_w  [3*H*D][4]    bf16: depthwise conv weights, q channels then k then
+ *                        v; tap 3 multiplies the current token, tap 0 the
+ *                        oldest cached one.  No bias.
+ *  conv_in [M][3][3*H*D] bf16: the last three raw inputs per channel,
+ *                        tap 0 oldest (the channel index runs over q|k|v).
+ *  conv_out same shape:  receives (tap1, tap2, x).  May be the SAME pointer
+ *                        as conv_in (in-place); must not partially overlap.
+ *                        Distinct buffers let the library split a head over
+ *                        several workgroups when M*H is small.
+ *  alpha   [M][H][D]     f32 per key-channel decay, in [0, 1] (linear, not log).
+ *  beta    [M][H]        f32 write strength, in [0, 1].
+ *  scale   q scale applied after the norm (1/sqrt(D) as in fla's decode; 1
+ *          for Eq. 1 as printed).  Must be finite.
+ *  o       [M][H][D]     bf16 output, o = S'^T q^ computed from the unrounded
+ *                        f32 new state and rounded once.
+ *
+ * state, o and conv_out must not overlap each other or any input (except
+ * conv_out == conv_in exactly).  Returns a KDA_* status.
+ */
+int kda_decode_step(int M, int H, int D, int state_dtype,
+                    void *state, const void *x_qkv, const void *conv_w,
+                    const void *conv_in, void *conv_out,
+                    const float *alpha, const float *beta, float scale,
+                    void *o, void *stream);
+
+/*
+ * kda_decode_step_split -- kda_decode_step with an explicit work split:
+ * `nsplit` workgroups per head, each owning D/nsplit value columns.  nsplit
+ * is 1, 2 or 4; values above 1 need D == 128 and conv_out != conv_in (the
+ * workgroups of a head all read the head's q/k conv taps).  Results are
+ * bitwise identical for every nsplit.  kda_decode_step picks nsplit itself
+ * from M*H and the device's compute-unit count.  Returns a KDA_* status
+ * (KDA_ERR_ARG for an nsplit it cannot honour).
+ */
+int kda_decode_step_split(int M, int H, int D, int state_dtype,
+                          void *state, const void *x_qkv, const void *conv_w,
+                          const void *conv_in, void *conv_out,
+                          const float *alpha, const float *beta, float scale,
+                          void *o, void *stream, int nsplit);
+
+/*
+ * kda_conv_step -- the conv stage alone, over C independent channels
+ * ("GLM-5.3 deep dive", 8.2.4 step 2; one launch over all q|k|v channels).
+ *
+ *  x        [M][C]     bf16 current token.
+ *  conv_w   [C][4]     bf16 weights (tap 3 = current token).
+ *  conv_in  [M][3][C]  bf16 cached taps, tap 0 oldest.
+ *  conv_out [M][3][C]  bf16 shifted taps (tap1, tap2, x); may equal conv_in.
+ *  y        [M][C]     f32 SiLU(conv) output.
+ *
+ * C must be a multiple of 8.  Returns a KDA_* status.
+ */
+int kda_conv_step(int M, int C, const void *x, const void *conv_w,
+                  const void *conv_in, void *conv_out, float *y, void *stream);
+
+/*
+ * kda_recurrent_step -- steps 2 and 3 alone, from post-conv (post-SiLU) f32
+ * q|k|v: L2 norm, q scale, gated delta update and readout ("GLM-5.3 deep
+ * dive", 8.2.3 Eq. 1 and 8.2.6).  kda_conv_step followed by this call
+ * computes what kda_decode_step computes.
+ *
+ *  qkv [M][3][H*D] f32; state, alpha, beta, scale, o as kda_decode_step.
+ *  Returns a KDA_* status.
+ */
+int kda_recurrent_step(int M, int H, int D, int state_dtype, void *state,
+                       const float *qkv, const float *alpha, const float *beta,
+                       float scale, void *o, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

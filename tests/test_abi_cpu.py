@@ -1,0 +1,158 @@
+"""The C-ABI library loads, exports what include/kda.h declares, and rejects
+bad arguments on the host before touching the GPU (no GPU needed).
+
+Every call below is built to FAIL validation: the pointers are fake and are
+never dereferenced.  No call here may pass validation, or it would launch.
+"""
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import hybrid_linear_attention_kda_amd as kda
+from hybrid_linear_attention_kda_amd import kda as binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+GAP = 1 << 30  # fake buffers 1 GiB apart never overlap at these sizes
+
+
+def fake(i, misalign=0):
+    return (i + 1) * GAP + misalign
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), f"libkda.so does not export {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert kda.kda_version() == 10000
+    for code in range(8):
+        s = kda.kda_status_string(code)
+        assert s and s != "unknown status"
+    assert kda.kda_status_string(99) == "unknown status"
+
+
+def decode(lib, M=1, H=64, D=128, sdt=0, ptrs=None, scale=0.125, nsplit=None, mis=None):
+    p = [fake(i) for i in range(8)] if ptrs is None else list(ptrs)
+    if mis is not None:
+        p[mis] += 8
+    state, x, w, cin, cout, a, b, o = p
+    args = (M, H, D, sdt, state, x, w, cin, cout, a, b, scale, o, None)
+    if nsplit is None:
+        return lib.kda_decode_step(*args)
+    return lib.kda_decode_step_split(*args, nsplit)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), binding.KDA_ERR_ARG),
+    (dict(H=0), binding.KDA_ERR_SHAPE),
+    (dict(D=48), binding.KDA_ERR_SHAPE),
+    (dict(D=256), binding.KDA_ERR_SHAPE),
+    (dict(sdt=2), binding.KDA_ERR_DTYPE),
+    (dict(scale=math.nan), binding.KDA_ERR_ARG),
+    (dict(scale=math.inf), binding.KDA_ERR_ARG),
+    (dict(nsplit=3), binding.KDA_ERR_ARG),
+    (dict(nsplit=0), binding.KDA_ERR_ARG),
+    (dict(D=64, nsplit=2), binding.KDA_ERR_ARG),
+])
+def test_decode_argument_errors(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_decode_null_pointer(lib, which):
+    p = [fake(i) for i in range(8)]
+    p[which] = None
+    assert decode(lib, ptrs=p) == binding.KDA_ERR_NULL
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_decode_misaligned_pointer(lib, which):
+    assert decode(lib, mis=which) == binding.KDA_ERR_ALIGN
+
+
+def test_decode_empty_batch_touches_nothing(lib):
+    assert decode(lib, M=0, ptrs=[None] * 8) == binding.KDA_OK
+
+
+def test_decode_aliasing(lib):
+    base = [fake(i) for i in range(8)]
+    # state overlapping x
+    p = list(base); p[1] = p[0] + 4096
+    assert decode(lib, ptrs=p) == binding.KDA_ERR_ALIAS
+    # o inside the state
+    p = list(base); p[7] = p[0] + 1024
+    assert decode(lib, ptrs=p) == binding.KDA_ERR_ALIAS
+    # conv_out partially overlapping conv_in
+    p = list(base); p[4] = p[3] + 16
+    assert decode(lib, ptrs=p) == binding.KDA_ERR_ALIAS
+    # conv_out overlapping alpha
+    p = list(base); p[4] = p[5]
+    assert decode(lib, ptrs=p) == binding.KDA_ERR_ALIAS
+    # exact in-place conv state is allowed, but a split above 1 is not then
+    p = list(base); p[4] = p[3]
+    assert decode(lib, ptrs=p, nsplit=2) == binding.KDA_ERR_ARG
+
+
+def test_conv_step_errors(lib):
+    p = [fake(i) for i in range(5)]
+    assert lib.kda_conv_step(-1, 64, *p, None) == binding.KDA_ERR_ARG
+    assert lib.kda_conv_step(1, 12, *p, None) == binding.KDA_ERR_ARG
+    assert lib.kda_conv_step(1, 0, *p, None) == binding.KDA_ERR_ARG
+    assert lib.kda_conv_step(0, 64, None, None, None, None, None, None) == binding.KDA_OK
+    for i in range(5):
+        q = list(p); q[i] = None
+        assert lib.kda_conv_step(1, 64, *q, None) == binding.KDA_ERR_NULL
+        q = list(p); q[i] += 2
+        assert lib.kda_conv_step(1, 64, *q, None) == binding.KDA_ERR_ALIGN
+    q = list(p); q[4] = q[0]           # y over x
+    assert lib.kda_conv_step(1, 64, *q, None) == binding.KDA_ERR_ALIAS
+    q = list(p); q[3] = q[2] + 32      # conv_out partially over conv_in
+    assert lib.kda_conv_step(1, 64, *q, None) == binding.KDA_ERR_ALIAS
+
+
+def test_recurrent_step_errors(lib):
+    p = [fake(i) for i in range(5)]   # state, qkv, alpha, beta, o
+    def call(M=1, H=4, D=16, sdt=0, ptrs=p, scale=1.0):
+        s, q, a, b, o = ptrs
+        return lib.kda_recurrent_step(M, H, D, sdt, s, q, a, b, scale, o, None)
+    assert call(M=-2) == binding.KDA_ERR_ARG
+    assert call(D=8) == binding.KDA_ERR_SHAPE
+    assert call(sdt=5) == binding.KDA_ERR_DTYPE
+    assert call(scale=math.nan) == binding.KDA_ERR_ARG
+    assert call(M=0, ptrs=[None] * 5) == binding.KDA_OK
+    for i in range(5):
+        q = list(p); q[i] = None
+        assert call(ptrs=q) == binding.KDA_ERR_NULL
+        q = list(p); q[i] += 4
+        assert call(ptrs=q) == binding.KDA_ERR_ALIGN
+    q = list(p); q[4] = q[0] + 64
+    assert call(ptrs=q) == binding.KDA_ERR_ALIAS
+
+
+def test_binding_rejects_host_tensors():
+    M, H, D = 1, 2, 16
+    st = torch.zeros(M, H, D, D)
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(st, None, None, None, None, None, None, 1.0, None)
+    with pytest.raises(ValueError):
+        kda.kda_recurrent_step(st, None, None, None, 1.0, None)
+    with pytest.raises(ValueError):
+        kda.kda_conv_step(torch.zeros(1, 8, dtype=torch.bfloat16), None, None, None, None)
