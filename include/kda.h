@@ -26,7 +26,8 @@
  * - Every argument check happens on the host before any HIP call, so an
  *   invalid call returns its status without touching the GPU.
  * - M == 0 is an empty batch: KDA_OK, nothing is read or written.
- * - Results are bitwise deterministic for a given input, shape and device.
+ * - Results are bitwise deterministic for a given input, shape, work split
+ *   and device.
  * - Values outside the stated ranges (alpha, beta not in [0, 1], NaN) are the
  *   caller's contract and are not checked on the device.
  * - Rounding to bf16 is round-to-nearest-even; all arithmetic is f32.
@@ -95,8 +96,10 @@ int kda_decode_step(int M, int H, int D, int state_dtype,
  * kda_decode_step_split -- kda_decode_step with an explicit work split:
  * `nsplit` workgroups per head, each owning D/nsplit value columns.  nsplit
  * is 1, 2 or 4; values above 1 need D == 128 and conv_out != conv_in (the
- * workgroups of a head all read the head's q/k conv taps).  Results are
- * bitwise identical for every nsplit.  kda_decode_step picks nsplit itself
+ * workgroups of a head all read the head's q/k conv taps).  The split
+ * changes the order of the f32 sums over key rows, so results for different
+ * nsplit agree to f32 rounding, not bit for bit (each one is deterministic).
+ * The conv state is bit-identical for every nsplit.  kda_decode_step picks nsplit itself
  * from M*H and the device's compute-unit count.  Returns a KDA_* status
  * (KDA_ERR_ARG for an nsplit it cannot honour).
  */

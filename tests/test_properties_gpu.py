@@ -44,14 +44,26 @@ def test_bitwise_deterministic(state_dtype):
 
 
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-def test_split_is_bitwise_identical(state_dtype):
-    wl = kda_synth.custom("split", 2, 64, 128, steps=3)
-    ref, oref = run(wl, state_dtype, 3, nsplit=1, inplace=False)
+def test_split_agrees_to_rounding(orc, state_dtype):
+    """Splitting a head's value columns over 2 or 4 workgroups changes only the
+    order of the f32 sums over key rows: the conv state is bit-identical, the
+    state and output agree to f32 rounding (plus one bf16 ulp where stored as
+    bf16), and every split matches the oracle."""
+    wl = kda_synth.custom("split", 2, 64, 128, steps=1)
+    ref, oref = run(wl, state_dtype, 1, nsplit=1, inplace=False)
+    S0 = host(kda_synth.initial_state(wl, 0, DEV, state_dtype))
+    lay0 = Layer(wl, 0, DEV, state_dtype)
+    inp = kda_synth.step_inputs(wl, 0, 0, DEV)
+    S_ref, _, o_ref = orc.decode_step(S0, host(inp["x"]), host(lay0.conv_w), host(lay0.conv),
+                                      host(inp["alpha"]), host(inp["beta"]), wl.scale)
+    tol_s = 1e-6 if state_dtype == "f32" else 2 ** -7
     for ns in (2, 4):
-        lay, outs = run(wl, state_dtype, 3, nsplit=ns, inplace=False)
-        assert torch.equal(lay.state, ref.state), f"nsplit={ns} state"
-        assert all(torch.equal(x, y) for x, y in zip(outs, oref)), f"nsplit={ns} output"
+        lay, outs = run(wl, state_dtype, 1, nsplit=ns, inplace=False)
         assert torch.equal(lay.conv, ref.conv), f"nsplit={ns} conv state"
+        assert rel_err(host(lay.state), host(ref.state)) <= tol_s, f"nsplit={ns} state"
+        assert rel_err(host(outs[0]), host(oref[0])) <= 2 ** -7, f"nsplit={ns} output"
+        assert rel_err(host(outs[0]), o_ref) <= TOL_O
+        assert rel_err(host(lay.state), S_ref) <= (1e-5 if state_dtype == "f32" else 4e-3)
 
 
 def test_inplace_conv_equals_pingpong():
@@ -73,10 +85,13 @@ def test_side_stream_equals_default_stream():
 
 
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("D", [16, 128])
-def test_fused_equals_conv_then_recurrent(state_dtype, D):
-    wl = kda_synth.custom("unfused", 3, 8, D, steps=2)
-    fused = Layer(wl, 0, DEV, state_dtype)
+@pytest.mark.parametrize("M,H,D", [(3, 8, 16), (3, 8, 128), (16, 64, 128)])
+def test_fused_equals_conv_then_recurrent(state_dtype, M, H, D):
+    """Bitwise, when both paths get the same work split: the fused call uses
+    distinct conv buffers so that, like the recurrent entry, it may split a
+    head when M*H is small."""
+    wl = kda_synth.custom("unfused", M, H, D, steps=2)
+    fused = Layer(wl, 0, DEV, state_dtype, inplace=False)
     split = Layer(wl, 0, DEV, state_dtype)
     C = 3 * wl.H * D
     y = torch.empty((wl.M, C), dtype=torch.float32, device=DEV)
