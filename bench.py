@@ -291,7 +291,7 @@ def main():
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBS,
         "traffic": stored_traffic(head["alg_bytes_per_launch"]),
-        "kernel": "decode_kernel<float, D=128, NSPLIT=1, NWAVES=4, VEC=4>",
+        "kernel": "decode_kernel<float, D=128, NSPLIT=1, NWAVES=16, VEC=4>",
         "alg_bytes_per_launch": head["alg_bytes_per_launch"],
         "avg_launch_us": avg_launch_s * 1e6,
     }

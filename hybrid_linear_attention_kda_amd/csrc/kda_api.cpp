@@ -45,17 +45,19 @@ bool checked_bytes(long M, long a, long b, long c, long bytes, size_t* out) {
 
 int map_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-// Workgroups per head.  A head is one workgroup (64 KiB of f32 state) unless
-// M*H is too small to fill the device, in which case its value columns are
-// split.  Splitting needs distinct conv buffers: the split workgroups of a head
-// all read the head's q/k taps, so none may overwrite them in place.
-int choose_split(int M, int H, int D, bool conv_in_place) {
+// Workgroups per head.  A head is one workgroup (its whole state) unless M*H
+// is below the device's compute-unit count, in which case its value columns
+// are split so that more CUs take part.  Splitting needs distinct conv
+// buffers: the split workgroups of a head all read the head's q/k taps, so
+// none may overwrite them in place.  bf16 state splits at most 2-way (a
+// 4-way split would leave 64-byte row segments, half a cache line).
+int choose_split(int M, int H, int D, int sdt, bool conv_in_place) {
     if (D != 128 || conv_in_place) return 1;
     const long units = (long)M * H;
     int cus = kda::device_cu_count();
     if (cus <= 0) cus = 256;
-    if (units >= 4L * cus) return 1;
-    if (units >= 2L * cus) return 2;
+    if (units >= cus) return 1;
+    if (sdt == KDA_STATE_BF16 || 2 * units >= cus) return 2;
     return 4;
 }
 
@@ -120,7 +122,7 @@ int run_decode(int M, int H, int D, int sdt, void* state, const void* x, const v
     if (rc != KDA_OK || M == 0) return rc;
     const bool in_place = cout == cin;
     if (nsplit == 0) {
-        nsplit = choose_split(M, H, D, in_place);
+        nsplit = choose_split(M, H, D, sdt, in_place);
     } else {
         if (nsplit != 1 && nsplit != 2 && nsplit != 4) return KDA_ERR_ARG;
         if (nsplit > 1 && (D != 128 || in_place)) return KDA_ERR_ARG;
@@ -195,7 +197,7 @@ int kda_recurrent_step(int M, int H, int D, int state_dtype, void* state, const 
     if (overlap(rs, ro)) return KDA_ERR_ALIAS;
     kda::StepArgs a{};
     a.M = M; a.H = H; a.D = D; a.state_dtype = state_dtype;
-    a.nsplit = choose_split(M, H, D, false);
+    a.nsplit = choose_split(M, H, D, state_dtype, false);
     a.state = state; a.qkv = qkv; a.alpha = alpha; a.beta = beta; a.scale = scale; a.o = o;
     a.stream = stream;
     return map_hip(kda::launch_recurrent_step(a));

@@ -129,118 +129,183 @@ __device__ __forceinline__ float conv_silu(u32x2 w4, float t0, float t1, float t
 //
 // TS      state storage: float or uint16_t (bf16 bits)
 // D       head width (dk = dv)
-// NSPLIT  workgroups per head (each owns D/NSPLIT value columns)
+// NSPLIT  workgroups per head; each owns D/NSPLIT value columns and every key
+//         row of them, so the reductions over key rows stay in one workgroup
 // NWAVES  waves per workgroup
-// VEC     state elements per lane access
+// VEC     state elements per lane access (16 bytes for D = 128)
+// RMAP    0: a workgroup access covers consecutive rows (waves side by side);
+//         1: each wave owns a contiguous band of rows
 // FUSED   true: conv prologue from bf16 x + conv state; false: f32 q|k|v input
-template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, bool FUSED>
-__global__ __launch_bounds__(NWAVES * 64)
-void decode_kernel(const int H, TS* __restrict__ state,
-                   const uint16_t* __restrict__ x, const uint16_t* __restrict__ conv_w,
-                   const uint16_t* conv_in, uint16_t* conv_out,
-                   const float* __restrict__ qkv,
-                   const float* __restrict__ alpha, const float* __restrict__ beta,
-                   const float scale, uint16_t* __restrict__ o)
-{
-    constexpr int NT = NWAVES * 64;
-    constexpr int COLS = D / NSPLIT;          // value columns of this workgroup
-    constexpr int CG = COLS / VEC;            // lanes across one row segment
-    static_assert(COLS % VEC == 0 && 64 % CG == 0, "row segment must tile the wave");
-    constexpr int RPW = 64 / CG;              // rows per wave access
-    constexpr int RS = RPW * NWAVES;          // row slices per workgroup
-    static_assert(D % RS == 0, "row slices must tile the key axis");
-    constexpr int RPL = D / RS;               // rows per lane
-    constexpr int NCH = 2 * D + COLS;         // prologue channels: q, k, own v
-    constexpr int PIT = (NCH + NT - 1) / NT;  // prologue iterations per thread
+// XG      keep the NSPLIT workgroups of a head on one XCD (they read the same
+//         q/k inputs, which then come from that XCD's L2)
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP>
+struct Geo {
+    static constexpr int NT = NWAVES * 64;
+    static constexpr int COLS = D / NSPLIT;          // value columns of one workgroup
+    static constexpr int CG = COLS / VEC;            // lanes across one row segment
+    static_assert(COLS % VEC == 0 && CG >= 1 && 64 % CG == 0, "row segment must tile the wave");
+    static constexpr int RPW = 64 / CG;              // rows per wave access
+    static constexpr int RS = RPW * NWAVES;          // rows per workgroup access
+    static_assert(RS <= D && D % RS == 0, "row slices must tile the key axis");
+    static constexpr int RPL = D / RS;               // rows per lane
+    // the prologue works on groups of 4 channels (8 bytes of bf16)
+    static constexpr int GQ = D / 4;                 // q groups (then k, then own v)
+    static constexpr int NG = 2 * GQ + COLS / 4;     // prologue groups
+    static constexpr int QK_PER_SPLIT = 2 * GQ / NSPLIT;  // q/k groups each split writes back
+    static_assert(COLS % 4 == 0 && (2 * GQ) % NSPLIT == 0, "channel groups must tile the split");
+    static_assert(NG <= NT - D / 4, "prologue and alpha lanes must not overlap");
     typedef Chunk<TS, VEC> IO;
+    typedef typename IO::raw_t raw_t;
+    // key row of access t of (wave wv, row-in-wave rw)
+    static __device__ __forceinline__ int row(int wv, int rw, int t) {
+        return RMAP == 0 ? wv * RPW + rw + RS * t : (wv * RPL + t) * RPW + rw;
+    }
+};
 
+struct Ptrs {
+    int H;
+    void* state;
+    const uint16_t* x;
+    const uint16_t* conv_w;
+    const uint16_t* conv_in;
+    uint16_t* conv_out;
+    const float* qkv;
+    const float* alpha;
+    const float* beta;
+    float scale;
+    uint16_t* o;
+};
+
+// Workgroup b -> (unit = m*H + h, split).  Plain: the splits of a unit are
+// consecutive workgroups.  XG: workgroups are handed to the 8 XCDs round
+// robin, so within each run of 8*NSPLIT workgroups, those on one XCD are the
+// NSPLIT splits of one unit; a ragged tail of units falls back to plain.
+template <int NSPLIT, bool XG>
+__device__ __forceinline__ void block_unit(int b, int units, int& unit, int& split) {
+    if constexpr (XG && NSPLIT > 1) {
+        constexpr int GB = 8 * NSPLIT;
+        const int full = units >> 3;
+        if (b < full * GB) {
+            const int g = b / GB, r = b - g * GB;
+            unit = g * 8 + (r & 7);
+            split = r >> 3;
+            return;
+        }
+        b -= full * GB;
+        unit = full * 8 + b / NSPLIT;
+        split = b - (b / NSPLIT) * NSPLIT;
+        return;
+    }
+    unit = b / NSPLIT;
+    split = b - unit * NSPLIT;
+}
+
+// First channel (in [0, 3HD)) of prologue group g of head h, split `split`:
+// groups [0, GQ) are q, [GQ, 2GQ) k, the rest this split's v columns.
+template <class G, int D>
+__device__ __forceinline__ size_t group_channel(int g, int h, int split, size_t HD) {
+    const int tensor = g < G::GQ ? 0 : (g < 2 * G::GQ ? 1 : 2);
+    const int within = tensor < 2 ? 4 * (g - tensor * G::GQ) : split * G::COLS + 4 * (g - 2 * G::GQ);
+    return (size_t)tensor * HD + (size_t)h * D + within;
+}
+
+__device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(uint16_t* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// One workgroup per (unit, split): grid M*H*NSPLIT.
+//
+// Order inside the workgroup: the small prologue loads (4 channels per lane,
+// 8-byte accesses), then every state load of the lane (all in flight
+// together), then the conv + SiLU while the state is still arriving, then the
+// norms, the fade and both reductions as the state lands, one cross-wave
+// exchange, the delta correction, the readout, and the rank-1 write fused
+// into the stores.
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG>
+__global__ __launch_bounds__(NWAVES * 64)
+void decode_kernel(const Ptrs p, const int units)
+{
+    typedef Geo<TS, D, NSPLIT, NWAVES, VEC, RMAP> G;
+    constexpr int NT = G::NT, COLS = G::COLS, CG = G::CG, RPL = G::RPL, NG = G::NG;
     // conv outputs: q at [0, D), k at [D, 2D), this workgroup's v columns at
-    // [2D, 2D + COLS); the tail is scratch for threads past the last channel
-    __shared__ float s_z[PIT * NT];
+    // [2D, 2D + COLS)
+    __shared__ __attribute__((aligned(16))) float s_z[2 * D + COLS];
+    __shared__ __attribute__((aligned(16))) float s_a[D];
+    __shared__ float s_red[NWAVES > 1 ? NWAVES : 1][2][COLS];
+    __shared__ float s_d[COLS];
     float* const s_q = s_z;
     float* const s_k = s_z + D;
     float* const s_v = s_z + 2 * D;
-    __shared__ float s_a[D];
-    __shared__ float s_red[NWAVES > 1 ? NWAVES : 1][2][COLS];
-    __shared__ float s_d[COLS];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = tid >> 6;
-    const int split = (int)(blockIdx.x % NSPLIT);
-    const int unit = (int)(blockIdx.x / NSPLIT);        // m * H + h
-    const int m = unit / H;
-    const int h = unit - m * H;
-    const size_t HD = (size_t)H * D;
-    const size_t C3 = 3 * HD;
-
-    const int cg = lane % CG;
-    const int rw = lane / CG;
-    const int rs = wv * RPW + rw;
+    int unit, split;
+    block_unit<NSPLIT, XG>((int)blockIdx.x, units, unit, split);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int cg = lane % CG, rw = lane / CG;
     const int col0 = split * COLS + cg * VEC;
-    TS* st = state + (size_t)unit * D * D;
+    const int m = unit / p.H, h = unit - m * p.H;
+    const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
 
-    // ---- 1. prologue loads (small; issued first so they retire first) ----
-    // Loads are unconditional (a thread past the last channel re-reads the
-    // last one and discards it) so they issue as straight-line code.
-    u32x2 pw[PIT];
-    uint32_t bx[PIT], b0[PIT], b1[PIT], b2[PIT];   // raw bf16 bits (FUSED)
-    float px[PIT];                                  // f32 input (!FUSED)
-    size_t pch[PIT];
-#pragma unroll
-    for (int it = 0; it < PIT; ++it) {
-        const int c = min(tid + it * NT, NCH - 1);
-        const int tensor = c < D ? 0 : (c < 2 * D ? 1 : 2);
-        const int within = tensor < 2 ? c - tensor * D : split * COLS + (c - 2 * D);
-        pch[it] = (size_t)tensor * HD + (size_t)h * D + within;   // channel in [0, 3HD)
+    // ---- 1. prologue loads: lanes [0, NG) each own 4 channels; the last
+    // D/4 lanes of the workgroup load alpha, 4 values each ----
+    const bool pro = tid < NG;
+    const int ag = tid - (NT - D / 4);              // alpha group, valid if >= 0
+    size_t ch = 0;
+    u32x2 xv, t0, t1, t2;                           // raw bf16 (FUSED)
+    u32x4 w01, w23;                                 // 4 taps of 4 channels
+    f32x4 q0;                                       // f32 input (!FUSED)
+    f32x4 av;
+    if (pro) {
+        ch = group_channel<G, D>(tid, h, split, HD);
         if constexpr (FUSED) {
-            bx[it] = x[(size_t)m * C3 + pch[it]];
-            const uint16_t* ci = conv_in + (size_t)m * 3 * C3 + pch[it];
-            b0[it] = ci[0];
-            b1[it] = ci[C3];
-            b2[it] = ci[2 * C3];
-            pw[it] = *reinterpret_cast<const u32x2*>(conv_w + 4 * pch[it]);
+            xv = ld8(p.x + (size_t)m * C3 + ch);
+            const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
+            t0 = ld8(ci);
+            t1 = ld8(ci + C3);
+            t2 = ld8(ci + 2 * C3);
+            const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
+            w01 = wp[0];
+            w23 = wp[1];
         } else {
-            px[it] = qkv[(size_t)m * C3 + pch[it]];
+            q0 = *reinterpret_cast<const f32x4*>(p.qkv + (size_t)m * C3 + ch);
         }
     }
-    const float a_pre = alpha[(size_t)unit * D + min(tid, D - 1)];
-    const float b = beta[unit];
+    if (ag >= 0) av = *reinterpret_cast<const f32x4*>(p.alpha + (size_t)unit * D + 4 * ag);
+    const float b = p.beta[unit];
     // keep the scheduler from sinking these loads below the state loads:
     // the conv prologue then waits only for them, not for the state
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. issue every state load of this lane ----
-    typename IO::raw_t raw[RPL];
+    TS* const st = static_cast<TS*>(p.state) + (size_t)unit * D * D;
+    typename G::raw_t raw[RPL];
 #pragma unroll
-    for (int t = 0; t < RPL; ++t) raw[t] = IO::load(st + (size_t)(rs + RS * t) * D + col0);
+    for (int t = 0; t < RPL; ++t) raw[t] = G::IO::load(st + (size_t)G::row(wv, rw, t) * D + col0);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 3. conv + SiLU into LDS; advance the conv state ----
-    // (computed unconditionally so the compiler keeps the loads above)
-#pragma unroll
-    for (int it = 0; it < PIT; ++it) {
-        const int c = tid + it * NT;
-        float z;
+    if (pro) {
+        f32x4 z0;
         if constexpr (FUSED) {
-            z = conv_silu(pw[it], bf16_lo(b0[it]), bf16_lo(b1[it]), bf16_lo(b2[it]),
-                          bf16_lo(bx[it]));
-        } else {
-            z = px[it];
-        }
-        s_z[c] = z;
-        if constexpr (FUSED) {
-            // q/k taps are shared by the NSPLIT workgroups of a head: only
-            // split 0 writes them (the host keeps NSPLIT = 1 when in place).
-            if (c < NCH && (c >= 2 * D || split == 0)) {
-                uint16_t* co = conv_out + (size_t)m * 3 * C3 + pch[it];
-                co[0] = (uint16_t)b1[it];
-                co[C3] = (uint16_t)b2[it];
-                co[2 * C3] = (uint16_t)bx[it];
+            // channel 2c uses the low halves, channel 2c+1 the high halves;
+            // weights: 4 taps per channel, two channels per 16-byte word
+            z0 = f32x4{conv_silu(u32x2{w01.x, w01.y}, bf16_lo(t0.x), bf16_lo(t1.x), bf16_lo(t2.x), bf16_lo(xv.x)),
+                       conv_silu(u32x2{w01.z, w01.w}, bf16_hi(t0.x), bf16_hi(t1.x), bf16_hi(t2.x), bf16_hi(xv.x)),
+                       conv_silu(u32x2{w23.x, w23.y}, bf16_lo(t0.y), bf16_lo(t1.y), bf16_lo(t2.y), bf16_lo(xv.y)),
+                       conv_silu(u32x2{w23.z, w23.w}, bf16_hi(t0.y), bf16_hi(t1.y), bf16_hi(t2.y), bf16_hi(xv.y))};
+            // every split reads all q/k taps; each writes back its own share
+            // of them, and its own v taps (with NSPLIT > 1 the host requires
+            // conv_out != conv_in)
+            if (tid >= 2 * G::GQ || NSPLIT == 1 || tid / G::QK_PER_SPLIT == split) {
+                uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + ch;
+                st8(co, t1);
+                st8(co + C3, t2);
+                st8(co + 2 * C3, xv);
             }
+        } else {
+            z0 = q0;
         }
+        reinterpret_cast<f32x4*>(s_z)[tid] = z0;
     }
-    if (tid < D) s_a[tid] = a_pre;
+    if (ag >= 0) reinterpret_cast<f32x4*>(s_a)[ag] = av;
     lds_barrier();
 
     // ---- 4. L2 norms and k^.q^ (every wave reduces the same D values) ----
@@ -255,25 +320,26 @@ void decode_kernel(const int H, TS* __restrict__ state,
     sqq = wave_sum(sqq);
     skk = wave_sum(skk);
     sqk = wave_sum(sqk);
-    const float rq = scale * rsqrtf(sqq + 1e-6f);
+    const float rq = p.scale * rsqrtf(sqq + 1e-6f);
     const float rk = rsqrtf(skk + 1e-6f);
     const float kq = sqk * rq * rk;                    // k^ . q^
 
     // ---- 5. fade, and the two reductions over this lane's rows ----
-    float sreg[RPL][VEC];
+    float sreg[RPL][VEC], kk[RPL];
     float u[VEC], wq[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) { u[e] = 0.0f; wq[e] = 0.0f; }
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
-        const int i = rs + RS * t;
-        const float a = s_a[i], kk = s_k[i] * rk, qq = s_q[i] * rq;
-        IO::unpack(raw[t], sreg[t]);
+        const int i = G::row(wv, rw, t);
+        const float a = s_a[i], qq = s_q[i] * rq;
+        kk[t] = s_k[i] * rk;
+        G::IO::unpack(raw[t], sreg[t]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const float sv = sreg[t][e] * a;
             sreg[t][e] = sv;
-            u[e] = fmaf(sv, kk, u[e]);
+            u[e] = fmaf(sv, kk[t], u[e]);
             wq[e] = fmaf(sv, qq, wq[e]);
         }
     }
@@ -289,7 +355,10 @@ void decode_kernel(const int H, TS* __restrict__ state,
 
     // ---- 6. delta correction and readout ----
     float d[VEC];
+    uint16_t* const ou = p.o + (size_t)unit * D + split * COLS;
     if constexpr (NWAVES > 1) {
+        // partial sums of every wave to LDS; one thread per column adds them,
+        // forms d and o; d goes back to every lane through LDS
         if (rw == 0) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -304,7 +373,7 @@ void decode_kernel(const int H, TS* __restrict__ state,
             for (int w = 0; w < NWAVES; ++w) { U += s_red[w][0][tid]; W += s_red[w][1][tid]; }
             const float dj = b * (s_v[tid] - U);
             s_d[tid] = dj;
-            o[(size_t)unit * D + split * COLS + tid] = (uint16_t)f32_to_bf16_rne(fmaf(dj, kq, W));
+            ou[tid] = (uint16_t)f32_to_bf16_rne(fmaf(dj, kq, W));
         }
         lds_barrier();
 #pragma unroll
@@ -315,19 +384,16 @@ void decode_kernel(const int H, TS* __restrict__ state,
         if (rw == 0) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                o[(size_t)unit * D + split * COLS + cg * VEC + e] =
-                    (uint16_t)f32_to_bf16_rne(fmaf(d[e], kq, wq[e]));
+                ou[cg * VEC + e] = (uint16_t)f32_to_bf16_rne(fmaf(d[e], kq, wq[e]));
         }
     }
 
     // ---- 7. rank-1 write and store ----
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
-        const int i = rs + RS * t;
-        const float kk = s_k[i] * rk;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) sreg[t][e] = fmaf(kk, d[e], sreg[t][e]);
-        IO::store(st + (size_t)i * D + col0, sreg[t]);
+        for (int e = 0; e < VEC; ++e) sreg[t][e] = fmaf(kk[t], d[e], sreg[t][e]);
+        G::IO::store(st + (size_t)G::row(wv, rw, t) * D + col0, sreg[t]);
     }
 }
 
@@ -373,44 +439,81 @@ void conv_kernel(const int M, const int C, const uint16_t* __restrict__ x,
 
 // ---------------------------------------------------------------- launch --
 
-template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, bool FUSED>
-static hipError_t launch_decode(const StepArgs& a) {
-    void* args[] = {(void*)&a.H, (void*)&a.state, (void*)&a.x, (void*)&a.conv_w,
-                    (void*)&a.conv_in, (void*)&a.conv_out, (void*)&a.qkv,
-                    (void*)&a.alpha, (void*)&a.beta, (void*)&a.scale, (void*)&a.o};
-    const dim3 grid((unsigned)((long)a.M * a.H * NSPLIT));
-    const dim3 block(NWAVES * 64);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<TS, D, NSPLIT, NWAVES, VEC, FUSED>),
-                           grid, block, args, 0, (hipStream_t)a.stream);
+static Ptrs make_ptrs(const StepArgs& a) {
+    Ptrs p;
+    p.H = a.H;
+    p.state = a.state;
+    p.x = static_cast<const uint16_t*>(a.x);
+    p.conv_w = static_cast<const uint16_t*>(a.conv_w);
+    p.conv_in = static_cast<const uint16_t*>(a.conv_in);
+    p.conv_out = static_cast<uint16_t*>(a.conv_out);
+    p.qkv = a.qkv;
+    p.alpha = a.alpha;
+    p.beta = a.beta;
+    p.scale = a.scale;
+    p.o = static_cast<uint16_t*>(a.o);
+    return p;
 }
 
-template <typename TS, int D, int VEC, int NWAVES, bool FUSED>
-static hipError_t dispatch_split(const StepArgs& a) {
-    if constexpr (D == 128) {
-        switch (a.nsplit) {
-        case 1: return launch_decode<TS, D, 1, NWAVES, VEC, FUSED>(a);
-        case 2: return launch_decode<TS, D, 2, NWAVES, VEC, FUSED>(a);
-        case 4: return launch_decode<TS, D, 4, NWAVES, VEC, FUSED>(a);
-        default: return hipErrorInvalidValue;
-        }
-    } else {
-        if (a.nsplit != 1) return hipErrorInvalidValue;
-        return launch_decode<TS, D, 1, NWAVES, VEC, FUSED>(a);
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, bool FUSED, bool XG, int RMAP = 0>
+static hipError_t launch_decode(const StepArgs& a) {
+    Ptrs p = make_ptrs(a);
+    int units = a.M * a.H;
+    void* args[] = {(void*)&p, (void*)&units};
+    const dim3 grid((unsigned)((long)units * NSPLIT));
+    const dim3 block(NWAVES * 64);
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&decode_kernel<TS, D, NSPLIT, NWAVES, VEC, RMAP, FUSED, XG>), grid,
+        block, args, 0, (hipStream_t)a.stream);
+}
+
+// D = 128 launch shapes, from measurement on MI355X (34 layers of distinct
+// state, DRAM-resident):
+//  f32, whole head per workgroup: 8 waves (8 rows x 4 columns per lane); 16
+//    waves (4 rows per lane) once there are >= 2048 heads to run.
+//  bf16, whole head per workgroup: 8 waves, each owning a band of 16 rows.
+//  column splits (small M*H only): 8 waves (f32, 2-way), else 4 waves.
+// A split leaves every workgroup a row segment of >= 128 bytes for f32 at
+// 2- and 4-way and bf16 at 2-way; bf16 at 4-way (64 bytes) is supported but
+// shares cache lines between workgroups and is never chosen by the library.
+template <bool FUSED>
+static hipError_t dispatch_wide_f32(const StepArgs& a) {
+    switch (a.nsplit) {
+    case 1:
+        return (long)a.M * a.H >= 2048 ? launch_decode<float, 128, 1, 16, 4, FUSED, false, 0>(a)
+                                       : launch_decode<float, 128, 1, 8, 4, FUSED, false, 0>(a);
+    case 2: return launch_decode<float, 128, 2, 8, 4, FUSED, true, 0>(a);
+    case 4: return launch_decode<float, 128, 4, 4, 4, FUSED, true, 0>(a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool FUSED>
+static hipError_t dispatch_wide_bf16(const StepArgs& a) {
+    switch (a.nsplit) {
+    case 1: return launch_decode<uint16_t, 128, 1, 8, 8, FUSED, false, 1>(a);
+    case 2: return launch_decode<uint16_t, 128, 2, 4, 8, FUSED, true, 0>(a);
+    case 4: return launch_decode<uint16_t, 128, 4, 4, 8, FUSED, true, 0>(a);
+    default: return hipErrorInvalidValue;
     }
 }
 
 template <bool FUSED>
 static hipError_t dispatch(const StepArgs& a) {
     const bool f32 = a.state_dtype == 0;
+    if (a.D != 128 && a.nsplit != 1) return hipErrorInvalidValue;
     switch (a.D) {
     case 16:
-        return f32 ? dispatch_split<float, 16, 4, 1, FUSED>(a) : dispatch_split<uint16_t, 16, 4, 1, FUSED>(a);
+        return f32 ? launch_decode<float, 16, 1, 1, 4, FUSED, false>(a)
+                   : launch_decode<uint16_t, 16, 1, 1, 4, FUSED, false>(a);
     case 32:
-        return f32 ? dispatch_split<float, 32, 4, 1, FUSED>(a) : dispatch_split<uint16_t, 32, 8, 1, FUSED>(a);
+        return f32 ? launch_decode<float, 32, 1, 1, 4, FUSED, false>(a)
+                   : launch_decode<uint16_t, 32, 1, 1, 8, FUSED, false>(a);
     case 64:
-        return f32 ? dispatch_split<float, 64, 4, 2, FUSED>(a) : dispatch_split<uint16_t, 64, 8, 2, FUSED>(a);
+        return f32 ? launch_decode<float, 64, 1, 2, 4, FUSED, false>(a)
+                   : launch_decode<uint16_t, 64, 1, 2, 8, FUSED, false>(a);
     case 128:
-        return f32 ? dispatch_split<float, 128, 4, 4, FUSED>(a) : dispatch_split<uint16_t, 128, 8, 4, FUSED>(a);
+        return f32 ? dispatch_wide_f32<FUSED>(a) : dispatch_wide_bf16<FUSED>(a);
     default:
         return hipErrorInvalidValue;
     }

@@ -215,6 +215,21 @@ def test_ragged_shapes(orc, M, H, D, state_dtype):
                                                teacher=state_dtype == "bf16")
 
 
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("inplace", [True, False], ids=["conv_inplace", "conv_pingpong"])
+def test_many_units_ragged(orc, state_dtype, inplace):
+    """M*H = 1600 heads: the whole-head launch at a size that is not a multiple
+    of 8, so the last workgroups of the grid cover a ragged tail of heads."""
+    wl = kda_synth.custom("many_units", 25, 64, 128, steps=3)
+    lay = Layer(wl, 0, DEV, state_dtype, inplace=inplace)
+    S_ref, cs_ref = host(lay.state), host(lay.conv)
+    for t in range(wl.steps):
+        S_ref, cs_ref, e = full_step_check(orc, lay, S_ref, cs_ref,
+                                           kda_synth.step_inputs(wl, 0, t, DEV), tol_state(state_dtype),
+                                           teacher=state_dtype == "bf16")
+    say(f"many units {state_dtype} inplace={inplace}: o {e[0]:.3e} state {e[1]:.3e}")
+
+
 def test_empty_batch():
     from hybrid_linear_attention_kda_amd import kda_decode_step
     e = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device=DEV)  # noqa: E731

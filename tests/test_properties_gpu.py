@@ -36,8 +36,9 @@ def run(wl, state_dtype, steps, nsplit=None, inplace=True, stream=None):
 
 
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-def test_bitwise_deterministic(state_dtype):
-    wl = kda_synth.custom("det", 4, 64, 128, steps=3)
+@pytest.mark.parametrize("M", [4, 32])
+def test_bitwise_deterministic(state_dtype, M):
+    wl = kda_synth.custom("det", M, 64, 128, steps=3)
     a, oa = run(wl, state_dtype, 3)
     b, ob = run(wl, state_dtype, 3)
     assert torch.equal(a.state, b.state) and all(torch.equal(x, y) for x, y in zip(oa, ob))
@@ -85,7 +86,7 @@ def test_side_stream_equals_default_stream():
 
 
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("M,H,D", [(3, 8, 16), (3, 8, 128), (16, 64, 128)])
+@pytest.mark.parametrize("M,H,D", [(3, 8, 16), (3, 8, 128), (16, 64, 128), (32, 64, 128)])
 def test_fused_equals_conv_then_recurrent(state_dtype, M, H, D):
     """Bitwise, when both paths get the same work split: the fused call uses
     distinct conv buffers so that, like the recurrent entry, it may split a
@@ -126,8 +127,9 @@ def test_conv_step_against_oracle(orc):
 
 
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-def test_recurrent_step_against_oracle(orc, state_dtype):
-    M, H, D = 4, 64, 128
+@pytest.mark.parametrize("M", [4, 25])
+def test_recurrent_step_against_oracle(orc, state_dtype, M):
+    H, D = 64, 128
     wl = kda_synth.custom("rec", M, H, D)
     S = kda_synth.initial_state(wl, 0, DEV, state_dtype)
     g = torch.Generator(device=DEV).manual_seed(9)
