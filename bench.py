@@ -160,27 +160,47 @@ def measure(wl, state_dtype, steps, warmup, n_inputs):
     return out
 
 
-def copy_ceiling(gib=4.0):
-    """Plain device-to-device copy of `gib` GiB (1:1 read:write): the
-    achievable HBM ceiling for a stream that reads and writes equal bytes."""
+def stream_ceiling(chunk_bytes, layers, steps, warmup=3):
+    """The probe kernels (``libkda_probe.so``) over `layers` distinct chunks of
+    `chunk_bytes` each, one launch per chunk as the decode step launches one
+    per layer: the achievable rate of the decode's access contract.
+    Returns {"rmw": GB/s, "copy": GB/s, "rmw_avg_launch_us": ...}; GB/s
+    counts bytes read + written."""
     import torch
-    n = int(gib * (1 << 30)) // 4
-    a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    s.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e.record()
-    e.synchronize()
-    sec = s.elapsed_time(e) / 1e3 / reps
-    del a, b
+
+    from hybrid_linear_attention_kda_amd import probe
+    plib = probe.load()
+    n = chunk_bytes // 4
+    buf = torch.ones(layers * n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(buf)
+    stream = torch.cuda.Stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    chunks = [(buf.data_ptr() + i * chunk_bytes, dst.data_ptr() + i * chunk_bytes) for i in range(layers)]
+
+    def rmw():
+        for a, _ in chunks:
+            assert plib.kda_probe_rmw(ctypes.c_void_p(a), chunk_bytes, 1.0, sp) == 0
+
+    def copy():
+        for a, b in chunks:
+            assert plib.kda_probe_copy(ctypes.c_void_p(a), ctypes.c_void_p(b), chunk_bytes, sp) == 0
+
+    out = {}
+    for name, fn in (("rmw", rmw), ("copy", copy)):
+        for _ in range(warmup):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(steps):
+            fn()
+        e.record(stream)
+        e.synchronize()
+        sec = s.elapsed_time(e) / 1e3
+        out[name] = 2 * chunk_bytes * layers * steps / sec / 1e9
+        out[name + "_avg_launch_us"] = sec / (layers * steps) * 1e6
+    del buf, dst
     torch.cuda.empty_cache()
-    return 2 * n * 4 / sec / 1e9
+    return out
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -218,6 +238,67 @@ def cpu_baseline(wl, budget_s=12.0):
     }
 
 
+def _counter_means(run_dir, counter):
+    """{kernel name: (mean counter value, mean grid size, dispatches)} from a
+    rocprofv3 --pmc CSV directory (values averaged over dispatches)."""
+    import csv
+    import glob
+    import collections
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
+    acc = collections.defaultdict(lambda: [0.0, 0.0, 0])
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                a = acc[row["Kernel_Name"]]
+                a[0] += float(row["Counter_Value"])
+                a[1] += float(row["Grid_Size"])
+                a[2] += 1
+    return {k: (v[0] / v[2], v[1] / v[2], v[2]) for k, v in acc.items()}
+
+
+def traffic_from_counters(fetch_dir, write_dir):
+    """HBM bytes per headline decode launch from FETCH_SIZE and WRITE_SIZE,
+    each scaled by what the same counter reads for the probe's in-place rmw
+    (grid size x 16 bytes read and the same written), and stored with the
+    kernel source's hash so that a later kernel change voids it."""
+    decode_key = "decode_kernel<float, 128, 1, 16, 4"
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(table, key):
+        hits = [(k, v) for k, v in table.items() if key in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {key!r}, found {[k for k, _ in hits]}")
+        return hits[0][1]
+
+    f_dec, f_probe = pick(fetch, decode_key), pick(fetch, "rmw_kernel")
+    w_dec, w_probe = pick(write, decode_key), pick(write, "rmw_kernel")
+    probe_bytes = f_probe[1] * 16                      # grid size x 16-byte chunk
+    k_fetch = probe_bytes / (f_probe[0] * 1024)        # true bytes per counted byte
+    k_write = probe_bytes / (w_probe[0] * 1024)
+    read_b = f_dec[0] * 1024 * k_fetch
+    write_b = w_dec[0] * 1024 * k_write
+    rec = {
+        "kernel": decode_key + ", ...>",
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "traffic_bytes_per_launch": read_b + write_b,
+        "read_bytes_per_launch": read_b,
+        "write_bytes_per_launch": write_b,
+        "fetch_size_kib_per_launch": f_dec[0],
+        "write_size_kib_per_launch": w_dec[0],
+        "decode_dispatches": [f_dec[2], w_dec[2]],
+        "calibration": {"probe": "kda_probe_rmw", "probe_bytes_each_way": probe_bytes,
+                        "fetch_size_kib": f_probe[0], "write_size_kib": w_probe[0],
+                        "fetch_scale": k_fetch, "write_scale": k_write},
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def stored_traffic(alg_bytes):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
     if the kernel source changed since they were taken."""
@@ -238,8 +319,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--no-copy", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then "
+                         "WRITE_SIZE) into HBM bytes per decode launch, calibrated on the "
+                         "probe kernel's dispatches, and write " + os.path.relpath(TRAFFIC_FILE, ROOT))
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_counters(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the KDA decode step shards by stream with no "
               f"communication, so --gpus {args.gpus} is not run here.", file=sys.stderr)
@@ -276,9 +364,10 @@ def main():
             log(f"  {name} {sdt}: {r['launch']} {r['ms_per_layer'] * 1e3:.2f} us/layer "
                 f"{r['state_GBps']:.0f} GB/s")
 
-    copy_gbs = None if args.no_copy else copy_ceiling()
-    if copy_gbs:
-        log(f"  copy ceiling {copy_gbs:.0f} GB/s")
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = stream_ceiling(wl.state_bytes("f32"), wl.layers, max(5, args.steps // 10))
+        log(f"  probe ceiling: in-place rmw {ceiling['rmw']:.0f} GB/s, copy {ceiling['copy']:.0f} GB/s")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
@@ -316,7 +405,11 @@ def main():
         "ms_per_layer": head["ms_per_layer"],
         "frac_hbm_peak_state": head["state_GBps"] / HBM_PEAK_GBS,
         "modes": head["modes"],
-        "copy_ceiling_GBps": copy_gbs,
+        "stream_ceiling": None if ceiling is None else {
+            "rmw_GBps": ceiling["rmw"], "copy_GBps": ceiling["copy"],
+            "kernel": "kda_probe_rmw / kda_probe_copy: 512 threads, one 16-byte non-temporal "
+                      "chunk per lane, one launch per 128 MiB layer chunk, 34 chunks",
+            "decode_alg_over_rmw": achieved / ceiling["rmw"]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "secondary": secondary,

@@ -1,9 +1,11 @@
-"""Build ``libkda.so`` (the gfx950 HIP library behind ``include/kda.h``).
+"""Build ``libkda.so`` (the gfx950 HIP library behind ``include/kda.h``) and
+``libkda_probe.so`` (the measurement probes behind ``include/kda_probe.h``).
 
     python -m hybrid_linear_attention_kda_amd.build
 
-Compiles ``csrc/kda_kernels.hip`` and ``csrc/kda_api.cpp`` with hipcc for
-gfx950 only.  Packed-FP32 instructions are switched off for device code.
+Compiles ``csrc/kda_kernels.hip`` and ``csrc/kda_api.cpp``, and separately
+``csrc/kda_probe.hip``, with hipcc for gfx950 only.  Packed-FP32
+instructions are switched off for device code.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libkda.so")
 SOURCES = [os.path.join(CSRC, "kda_kernels.hip"), os.path.join(CSRC, "kda_api.cpp")]
 HEADERS = [os.path.join(INCLUDE, "kda.h"), os.path.join(CSRC, "kda_launch.h")]
+PROBE_LIBRARY = os.path.join(PKG, "libkda_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "kda_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,10 +33,9 @@ FLAGS = [
 ]
 
 
-def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile the library to ``output``; returns its path."""
+def _compile(sources: list[str], output: str, extra: list[str] | None, verbose: bool) -> str:
     tmp = output + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), f"-I{INCLUDE}", f"-I{CSRC}", *SOURCES, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *(extra or []), f"-I{INCLUDE}", f"-I{CSRC}", *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,11 +46,19 @@ def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool =
     return output
 
 
+def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile the decode library to ``output`` and the probe library beside
+    the package; returns the decode library's path."""
+    _compile(SOURCES, output, extra, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIBRARY, None, verbose)
+    return output
+
+
 def is_stale(path: str = LIBRARY) -> bool:
-    if not os.path.exists(path):
+    if not os.path.exists(path) or not os.path.exists(PROBE_LIBRARY):
         return True
-    t = os.path.getmtime(path)
-    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)
+    t = min(os.path.getmtime(path), os.path.getmtime(PROBE_LIBRARY))
+    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS + PROBE_SOURCES)
 
 
 if __name__ == "__main__":

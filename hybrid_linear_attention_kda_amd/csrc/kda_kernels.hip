@@ -17,8 +17,8 @@
 //  * One workgroup owns one head (or 1/NSPLIT of its value columns).  Each
 //    lane owns VEC consecutive value columns of RPL key rows and holds them in
 //    VGPRs for the whole step, so the state is read once and written once and
-//    LDS never holds it (LDS per workgroup stays ~3 KiB: occupancy is set by
-//    VGPRs only).
+//    LDS never holds it (LDS holds the q/k/v/alpha vectors and per-wave
+//    partial sums, at most ~19 KiB at 16 waves: occupancy is set by VGPRs).
 //  * Loads and stores of the state are 16 bytes per lane; a wave covers whole
 //    contiguous rows (512 B f32 / 256 B bf16), so every access is coalesced.
 //  * All state loads are issued before the conv prologue is computed; the
@@ -154,6 +154,8 @@ struct Geo {
     static constexpr int QK_PER_SPLIT = 2 * GQ / NSPLIT;  // q/k groups each split writes back
     static_assert(COLS % 4 == 0 && (2 * GQ) % NSPLIT == 0, "channel groups must tile the split");
     static_assert(NG <= NT - D / 4, "prologue and alpha lanes must not overlap");
+    static constexpr int IO_VEC = VEC;               // state elements per lane access
+    static constexpr int NSPLIT_ = NSPLIT;
     typedef Chunk<TS, VEC> IO;
     typedef typename IO::raw_t raw_t;
     // key row of access t of (wave wv, row-in-wave rw)
@@ -212,103 +214,124 @@ __device__ __forceinline__ size_t group_channel(int g, int h, int split, size_t 
 __device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st8(uint16_t* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
-// One workgroup per (unit, split): grid M*H*NSPLIT.
-//
-// Order inside the workgroup: the small prologue loads (4 channels per lane,
-// 8-byte accesses), then every state load of the lane (all in flight
-// together), then the conv + SiLU while the state is still arriving, then the
-// norms, the fade and both reductions as the state lands, one cross-wave
-// exchange, the delta correction, the readout, and the rank-1 write fused
-// into the stores.
-template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG>
-__global__ __launch_bounds__(NWAVES * 64)
-void decode_kernel(const Ptrs p, const int units)
-{
-    typedef Geo<TS, D, NSPLIT, NWAVES, VEC, RMAP> G;
-    constexpr int NT = G::NT, COLS = G::COLS, CG = G::CG, RPL = G::RPL, NG = G::NG;
-    // conv outputs: q at [0, D), k at [D, 2D), this workgroup's v columns at
-    // [2D, 2D + COLS)
-    __shared__ __attribute__((aligned(16))) float s_z[2 * D + COLS];
-    __shared__ __attribute__((aligned(16))) float s_a[D];
-    __shared__ float s_red[NWAVES > 1 ? NWAVES : 1][2][COLS];
-    __shared__ float s_d[COLS];
-    float* const s_q = s_z;
-    float* const s_k = s_z + D;
-    float* const s_v = s_z + 2 * D;
+// One unit's small inputs, held in VGPRs from their loads to the conv.
+struct Pro {
+    u32x2 xv, t0, t1, t2;      // raw bf16 x and taps of 4 channels (FUSED)
+    u32x4 w01, w23;            // their 4 conv taps each
+    f32x4 q0;                  // f32 q|k|v of 4 channels (!FUSED)
+    f32x4 av;                  // 4 alpha values
+    float b;                   // beta of the unit
+};
 
-    int unit, split;
-    block_unit<NSPLIT, XG>((int)blockIdx.x, units, unit, split);
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int cg = lane % CG, rw = lane / CG;
-    const int col0 = split * COLS + cg * VEC;
+// LDS of one workgroup: conv outputs (q at [0, D), k at [D, 2D), this
+// workgroup's v columns at [2D, 2D + COLS)), alpha, per-wave partial sums,
+// and the delta vector.
+template <class G, int D>
+struct Smem {
+    __attribute__((aligned(16))) float z[2 * D + G::COLS];
+    __attribute__((aligned(16))) float a[D];
+    float red[G::NT / 64][2][G::COLS];
+    float d[G::COLS];
+    float w[G::COLS];
+};
+
+// Issue the small loads of unit `unit`: lanes [0, NG) own 4 channels each
+// (q, k, this split's v); the last D/4 lanes of the workgroup load alpha.
+template <class G, int D, bool FUSED>
+__device__ __forceinline__ void load_pro(Pro& in, const Ptrs& p, int unit, int split) {
+    const int tid = threadIdx.x;
+    const int m = unit / p.H, h = unit - m * p.H;
+    const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
+    if (tid < G::NG) {
+        const size_t ch = group_channel<G, D>(tid, h, split, HD);
+        if constexpr (FUSED) {
+            in.xv = ld8(p.x + (size_t)m * C3 + ch);
+            const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
+            in.t0 = ld8(ci);
+            in.t1 = ld8(ci + C3);
+            in.t2 = ld8(ci + 2 * C3);
+            const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
+            in.w01 = wp[0];
+            in.w23 = wp[1];
+        } else {
+            in.q0 = *reinterpret_cast<const f32x4*>(p.qkv + (size_t)m * C3 + ch);
+        }
+    }
+    const int ag = tid - (G::NT - D / 4);
+    if (ag >= 0) in.av = *reinterpret_cast<const f32x4*>(p.alpha + (size_t)unit * D + 4 * ag);
+    in.b = p.beta[unit];
+}
+
+// Issue every state load of this lane for unit `unit`.  live == false issues
+// the same number of loads, all from the unit's first row segment (a
+// placeholder that keeps the instruction stream, and its wait counts, fixed).
+template <typename TS, class G, int D>
+__device__ __forceinline__ void load_state(typename G::raw_t (&raw)[G::RPL], const Ptrs& p, int unit,
+                                           int split, bool live) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cg = lane % G::CG, rw = lane / G::CG;
+    const TS* st = static_cast<const TS*>(p.state) + (size_t)unit * D * D + split * G::COLS + cg * G::IO_VEC;
+#pragma unroll
+    for (int t = 0; t < G::RPL; ++t) raw[t] = G::IO::load(st + (live ? (size_t)G::row(wv, rw, t) * D : 0));
+}
+
+// Conv + SiLU of one unit's channels into LDS and the conv state shift;
+// alpha into LDS.  The caller places a barrier after it.
+template <class G, int D, bool FUSED>
+__device__ __forceinline__ void conv_unit(const Pro& in, const Ptrs& p, int unit, int split, Smem<G, D>& sm) {
+    constexpr int NT = G::NT;
+    const int tid = threadIdx.x;
     const int m = unit / p.H, h = unit - m * p.H;
     const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
 
-    // ---- 1. prologue loads: lanes [0, NG) each own 4 channels; the last
-    // D/4 lanes of the workgroup load alpha, 4 values each ----
-    const bool pro = tid < NG;
-    const int ag = tid - (NT - D / 4);              // alpha group, valid if >= 0
-    size_t ch = 0;
-    u32x2 xv, t0, t1, t2;                           // raw bf16 (FUSED)
-    u32x4 w01, w23;                                 // 4 taps of 4 channels
-    f32x4 q0;                                       // f32 input (!FUSED)
-    f32x4 av;
-    if (pro) {
-        ch = group_channel<G, D>(tid, h, split, HD);
-        if constexpr (FUSED) {
-            xv = ld8(p.x + (size_t)m * C3 + ch);
-            const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
-            t0 = ld8(ci);
-            t1 = ld8(ci + C3);
-            t2 = ld8(ci + 2 * C3);
-            const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
-            w01 = wp[0];
-            w23 = wp[1];
-        } else {
-            q0 = *reinterpret_cast<const f32x4*>(p.qkv + (size_t)m * C3 + ch);
-        }
-    }
-    if (ag >= 0) av = *reinterpret_cast<const f32x4*>(p.alpha + (size_t)unit * D + 4 * ag);
-    const float b = p.beta[unit];
-    // keep the scheduler from sinking these loads below the state loads:
-    // the conv prologue then waits only for them, not for the state
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- 2. issue every state load of this lane ----
-    TS* const st = static_cast<TS*>(p.state) + (size_t)unit * D * D;
-    typename G::raw_t raw[RPL];
-#pragma unroll
-    for (int t = 0; t < RPL; ++t) raw[t] = G::IO::load(st + (size_t)G::row(wv, rw, t) * D + col0);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- 3. conv + SiLU into LDS; advance the conv state ----
-    if (pro) {
+    // ---- conv + SiLU into LDS; advance the conv state ----
+    if (tid < G::NG) {
         f32x4 z0;
         if constexpr (FUSED) {
             // channel 2c uses the low halves, channel 2c+1 the high halves;
             // weights: 4 taps per channel, two channels per 16-byte word
-            z0 = f32x4{conv_silu(u32x2{w01.x, w01.y}, bf16_lo(t0.x), bf16_lo(t1.x), bf16_lo(t2.x), bf16_lo(xv.x)),
-                       conv_silu(u32x2{w01.z, w01.w}, bf16_hi(t0.x), bf16_hi(t1.x), bf16_hi(t2.x), bf16_hi(xv.x)),
-                       conv_silu(u32x2{w23.x, w23.y}, bf16_lo(t0.y), bf16_lo(t1.y), bf16_lo(t2.y), bf16_lo(xv.y)),
-                       conv_silu(u32x2{w23.z, w23.w}, bf16_hi(t0.y), bf16_hi(t1.y), bf16_hi(t2.y), bf16_hi(xv.y))};
+            z0 = f32x4{conv_silu(u32x2{in.w01.x, in.w01.y}, bf16_lo(in.t0.x), bf16_lo(in.t1.x),
+                                 bf16_lo(in.t2.x), bf16_lo(in.xv.x)),
+                       conv_silu(u32x2{in.w01.z, in.w01.w}, bf16_hi(in.t0.x), bf16_hi(in.t1.x),
+                                 bf16_hi(in.t2.x), bf16_hi(in.xv.x)),
+                       conv_silu(u32x2{in.w23.x, in.w23.y}, bf16_lo(in.t0.y), bf16_lo(in.t1.y),
+                                 bf16_lo(in.t2.y), bf16_lo(in.xv.y)),
+                       conv_silu(u32x2{in.w23.z, in.w23.w}, bf16_hi(in.t0.y), bf16_hi(in.t1.y),
+                                 bf16_hi(in.t2.y), bf16_hi(in.xv.y))};
             // every split reads all q/k taps; each writes back its own share
             // of them, and its own v taps (with NSPLIT > 1 the host requires
             // conv_out != conv_in)
-            if (tid >= 2 * G::GQ || NSPLIT == 1 || tid / G::QK_PER_SPLIT == split) {
-                uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + ch;
-                st8(co, t1);
-                st8(co + C3, t2);
-                st8(co + 2 * C3, xv);
+            if (tid >= 2 * G::GQ || G::NSPLIT_ == 1 || tid / G::QK_PER_SPLIT == split) {
+                uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + group_channel<G, D>(tid, h, split, HD);
+                st8(co, in.t1);
+                st8(co + C3, in.t2);
+                st8(co + 2 * C3, in.xv);
             }
         } else {
-            z0 = q0;
+            z0 = in.q0;
         }
-        reinterpret_cast<f32x4*>(s_z)[tid] = z0;
+        reinterpret_cast<f32x4*>(sm.z)[tid] = z0;
     }
-    if (ag >= 0) reinterpret_cast<f32x4*>(s_a)[ag] = av;
-    lds_barrier();
+    const int ag = tid - (NT - D / 4);
+    if (ag >= 0) reinterpret_cast<f32x4*>(sm.a)[ag] = in.av;
+}
 
-    // ---- 4. L2 norms and k^.q^ (every wave reduces the same D values) ----
+// The rest of one unit, after conv_unit and a barrier: norms, fade and both
+// reductions, one cross-wave exchange, delta correction, readout, rank-1
+// write and the stores.
+template <typename TS, class G, int D>
+__device__ __forceinline__ void update_unit(float b, typename G::raw_t (&raw)[G::RPL], const Ptrs& p,
+                                            int unit, int split, Smem<G, D>& sm) {
+    constexpr int NT = G::NT, COLS = G::COLS, CG = G::CG, RPL = G::RPL, VEC = G::IO_VEC;
+    constexpr int NWAVES = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int cg = lane % CG, rw = lane / CG;
+    const int col0 = split * COLS + cg * VEC;
+    float* const s_q = sm.z;
+    float* const s_k = sm.z + D;
+    float* const s_v = sm.z + 2 * D;
+
+    // ---- L2 norms and k^.q^ (every wave reduces the same D values) ----
     float sqq = 0.0f, skk = 0.0f, sqk = 0.0f;
 #pragma unroll
     for (int i = lane; i < D; i += 64) {
@@ -324,7 +347,7 @@ void decode_kernel(const Ptrs p, const int units)
     const float rk = rsqrtf(skk + 1e-6f);
     const float kq = sqk * rq * rk;                    // k^ . q^
 
-    // ---- 5. fade, and the two reductions over this lane's rows ----
+    // ---- fade, and the two reductions over this lane's rows ----
     float sreg[RPL][VEC], kk[RPL];
     float u[VEC], wq[VEC];
 #pragma unroll
@@ -332,7 +355,7 @@ void decode_kernel(const Ptrs p, const int units)
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
         const int i = G::row(wv, rw, t);
-        const float a = s_a[i], qq = s_q[i] * rq;
+        const float a = sm.a[i], qq = s_q[i] * rq;
         kk[t] = s_k[i] * rk;
         G::IO::unpack(raw[t], sreg[t]);
 #pragma unroll
@@ -353,31 +376,37 @@ void decode_kernel(const Ptrs p, const int units)
         }
     }
 
-    // ---- 6. delta correction and readout ----
+    // ---- delta correction and readout ----
     float d[VEC];
     uint16_t* const ou = p.o + (size_t)unit * D + split * COLS;
     if constexpr (NWAVES > 1) {
-        // partial sums of every wave to LDS; one thread per column adds them,
-        // forms d and o; d goes back to every lane through LDS
+        // partial sums of every wave to LDS; one thread per column adds the
+        // u partials and forms d, another adds the w partials; d goes back
+        // to every lane through LDS, and o = w + d (k^.q^) is written after
+        static_assert(2 * COLS <= NT, "u and w sums need 2*COLS threads");
         if (rw == 0) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                s_red[wv][0][cg * VEC + e] = u[e];
-                s_red[wv][1][cg * VEC + e] = wq[e];
+                sm.red[wv][0][cg * VEC + e] = u[e];
+                sm.red[wv][1][cg * VEC + e] = wq[e];
             }
         }
         lds_barrier();
         if (tid < COLS) {
-            float U = 0.0f, W = 0.0f;
+            float U = 0.0f;
 #pragma unroll
-            for (int w = 0; w < NWAVES; ++w) { U += s_red[w][0][tid]; W += s_red[w][1][tid]; }
-            const float dj = b * (s_v[tid] - U);
-            s_d[tid] = dj;
-            ou[tid] = (uint16_t)f32_to_bf16_rne(fmaf(dj, kq, W));
+            for (int w = 0; w < NWAVES; ++w) U += sm.red[w][0][tid];
+            sm.d[tid] = b * (s_v[tid] - U);
+        } else if (tid < 2 * COLS) {
+            float W = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) W += sm.red[w][1][tid - COLS];
+            sm.w[tid - COLS] = W;
         }
         lds_barrier();
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) d[e] = s_d[cg * VEC + e];
+        for (int e = 0; e < VEC; ++e) d[e] = sm.d[cg * VEC + e];
+        if (tid < COLS) ou[tid] = (uint16_t)f32_to_bf16_rne(fmaf(sm.d[tid], kq, sm.w[tid]));
     } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) d[e] = b * (s_v[cg * VEC + e] - u[e]);
@@ -388,13 +417,38 @@ void decode_kernel(const Ptrs p, const int units)
         }
     }
 
-    // ---- 7. rank-1 write and store ----
+    // ---- rank-1 write and store ----
+    TS* const st = static_cast<TS*>(p.state) + (size_t)unit * D * D;
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) sreg[t][e] = fmaf(kk[t], d[e], sreg[t][e]);
         G::IO::store(st + (size_t)G::row(wv, rw, t) * D + col0, sreg[t]);
     }
+}
+
+// One workgroup per (unit, split): grid M*H*NSPLIT.  The small prologue
+// loads go first, then every state load of the lane (all in flight
+// together); the conv + SiLU runs while the state is still arriving.
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG>
+__global__ __launch_bounds__(NWAVES * 64)
+void decode_kernel(const Ptrs p, const int units)
+{
+    typedef Geo<TS, D, NSPLIT, NWAVES, VEC, RMAP> G;
+    __shared__ Smem<G, D> sm;
+    int unit, split;
+    block_unit<NSPLIT, XG>((int)blockIdx.x, units, unit, split);
+    Pro in;
+    load_pro<G, D, FUSED>(in, p, unit, split);
+    // keep the scheduler from sinking these loads below the state loads:
+    // the conv prologue then waits only for them, not for the state
+    __builtin_amdgcn_sched_barrier(0);
+    typename G::raw_t raw[G::RPL];
+    load_state<TS, G, D>(raw, p, unit, split, true);
+    __builtin_amdgcn_sched_barrier(0);
+    conv_unit<G, D, FUSED>(in, p, unit, split, sm);
+    lds_barrier();
+    update_unit<TS, G, D>(in.b, raw, p, unit, split, sm);
 }
 
 // -------------------------------------------------------------- conv step --

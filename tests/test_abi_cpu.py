@@ -156,3 +156,24 @@ def test_binding_rejects_host_tensors():
         kda.kda_recurrent_step(st, None, None, None, 1.0, None)
     with pytest.raises(ValueError):
         kda.kda_conv_step(torch.zeros(1, 8, dtype=torch.bfloat16), None, None, None, None)
+
+
+# ------------------------------------------------------- measurement probes --
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """libkda_probe.so exports what include/kda_probe.h declares; every call
+    here fails host validation (fake pointers, never dereferenced)."""
+    from hybrid_linear_attention_kda_amd import probe
+    text = open(os.path.join(ROOT, "include", "kda_probe.h")).read()
+    names = sorted(set(re.findall(r"^int\s*(\w+)\(", text, re.M)))
+    assert set(names) == set(probe.EXPORTS)
+    plib = probe.load()
+    for n in names:
+        assert hasattr(plib, n), f"libkda_probe.so does not export {n}"
+    assert plib.kda_probe_rmw(None, 8192, 1.0, None) == 1
+    assert plib.kda_probe_rmw(fake(0, 8), 8192, 1.0, None) == 4
+    assert plib.kda_probe_rmw(fake(0), 0, 1.0, None) == 6
+    assert plib.kda_probe_rmw(fake(0), 8192 + 16, 1.0, None) == 6
+    assert plib.kda_probe_copy(fake(0), None, 8192, None) == 1
+    assert plib.kda_probe_copy(fake(0), fake(0, 8), 8192, None) == 4
+    assert plib.kda_probe_copy(fake(0), fake(0) + 4096, 8192, None) == 5
+    assert plib.kda_probe_copy(fake(0), fake(1), 100, None) == 6
