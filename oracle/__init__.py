@@ -13,7 +13,9 @@ follows are cited in the C file:
   in fade / predict / correct / read order;
 * same page, 8.2.4: short causal convolution (kernel 4) with SiLU, L2 norm;
 * "At the 262k cap the DSA indexer costs 12x the sparse MLA it selects for",
-  "Geometry": depthwise conv, kernel 4, three cached taps.
+  "Geometry": depthwise conv, kernel 4, three cached taps;
+* "GLM-5.3 deep dive" 8.2.3 (the forget gate as fla computes it) and 8.2.4
+  (write strength, gated RMSNorm on the output).
 
 Parity pins for every routine live in ``tests/oracle_pins.py``.
 """
@@ -31,6 +33,11 @@ LIBRARY = os.path.join(HERE, "libkda_oracle.so")
 
 #: epsilon of the L2 norm, "GLM-5.3 deep dive" 8.2.6 implementation notes.
 L2NORM_EPS = 1e-6
+#: epsilon of the gated RMSNorm, "GLM-5.3 deep dive" 8.2.4 implementation notes.
+RMSNORM_EPS = 1e-5
+#: gate forms, "GLM-5.3 deep dive" 8.2.3: bounded sigmoid (GLM-5.3-Flash, lower
+#: bound -5) and fla's default softplus form.
+GATE_BOUNDED, GATE_SOFTPLUS = 0, 1
 
 _CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
            "-ffp-contract=off", "-fno-fast-math"]
@@ -80,6 +87,16 @@ class Oracle:
         lib.kda_oracle_recurrent_step.restype = i
         lib.kda_oracle_max_threads.argtypes = []
         lib.kda_oracle_max_threads.restype = i
+        lib.kda_oracle_gate.argtypes = [i, p, d, p, i, d, p]
+        lib.kda_oracle_gate.restype = None
+        lib.kda_oracle_beta.argtypes = [i, p, p]
+        lib.kda_oracle_beta.restype = None
+        lib.kda_oracle_gated_rmsnorm.argtypes = [i, p, p, p, d, p]
+        lib.kda_oracle_gated_rmsnorm.restype = None
+        lib.kda_oracle_decode_step_gated.argtypes = [i, i, i, p, p, p, p, p, p, p, p, p, i, d, d, d, p]
+        lib.kda_oracle_decode_step_gated.restype = i
+        lib.kda_oracle_layer_step.argtypes = [i, i, i, p, p, p, p, p, p, p, p, p, i, d, d, d, p, p, d, p]
+        lib.kda_oracle_layer_step.restype = i
         self.lib = lib
 
     def max_threads(self) -> int:
@@ -147,6 +164,74 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"kda_oracle_recurrent_step failed ({rc})")
         return S, o
+
+
+    # -- gate, write strength, output norm ------------------------------------
+    def gate(self, f, A_log, dt_bias, kind=GATE_BOUNDED, lower_bound=-5.0):
+        """One head: f, dt_bias [D], A_log scalar -> alpha [D]."""
+        f, b = _f64(f), _f64(dt_bias)
+        assert f.shape == b.shape and f.ndim == 1
+        out = np.empty_like(f)
+        self.lib.kda_oracle_gate(f.shape[0], _ptr(f), float(A_log), _ptr(b), int(kind),
+                                 float(lower_bound), _ptr(out))
+        return out
+
+    def beta(self, logit):
+        logit = _f64(logit)
+        out = np.empty_like(logit)
+        self.lib.kda_oracle_beta(logit.size, _ptr(logit), _ptr(out))
+        return out
+
+    def gated_rmsnorm(self, o, g, w, eps=RMSNORM_EPS):
+        """One head: o, g, w [D] -> y [D]."""
+        o, g, w = _f64(o), _f64(g), _f64(w)
+        assert o.shape == g.shape == w.shape and o.ndim == 1
+        y = np.empty_like(o)
+        self.lib.kda_oracle_gated_rmsnorm(o.shape[0], _ptr(o), _ptr(g), _ptr(w), float(eps), _ptr(y))
+        return y
+
+    def decode_step_gated(self, S, x, w, cs, f, A_log, dt_bias, beta_logit, scale,
+                          kind=GATE_BOUNDED, lower_bound=-5.0, eps=L2NORM_EPS):
+        """The fused step with raw gate inputs: f [M,H*D], A_log [H],
+        dt_bias [H*D], beta_logit [M,H]; the rest as decode_step.
+        Returns (S_new, cs_new, o)."""
+        S = _f64(S).copy()
+        M, H, D, _ = S.shape
+        x, w, cs = _f64(x), _f64(w), _f64(cs)
+        f, A_log, dt_bias, beta_logit = _f64(f), _f64(A_log), _f64(dt_bias), _f64(beta_logit)
+        assert f.shape == (M, H * D) and A_log.shape == (H,) and dt_bias.shape == (H * D,)
+        assert beta_logit.shape == (M, H) and x.shape == (M, 3, H * D)
+        cs_out = np.empty_like(cs)
+        o = np.empty((M, H, D))
+        rc = self.lib.kda_oracle_decode_step_gated(M, H, D, _ptr(S), _ptr(x), _ptr(w), _ptr(cs),
+                                                   _ptr(cs_out), _ptr(f), _ptr(A_log),
+                                                   _ptr(dt_bias), _ptr(beta_logit), int(kind),
+                                                   float(lower_bound), float(scale), float(eps),
+                                                   _ptr(o))
+        if rc != 0:
+            raise RuntimeError(f"kda_oracle_decode_step_gated failed ({rc})")
+        return S, cs_out, o
+
+    def layer_step(self, S, x, w, cs, f, A_log, dt_bias, beta_logit, scale, out_gate, norm_w,
+                   kind=GATE_BOUNDED, lower_bound=-5.0, eps=L2NORM_EPS, norm_eps=RMSNORM_EPS):
+        """decode_step_gated followed by the gated RMSNorm of every head:
+        out_gate [M,H*D], norm_w [D].  Returns (S_new, cs_new, y [M,H,D])."""
+        S = _f64(S).copy()
+        M, H, D, _ = S.shape
+        x, w, cs = _f64(x), _f64(w), _f64(cs)
+        f, A_log, dt_bias, beta_logit = _f64(f), _f64(A_log), _f64(dt_bias), _f64(beta_logit)
+        og, nw = _f64(out_gate), _f64(norm_w)
+        assert og.shape == (M, H * D) and nw.shape == (D,)
+        cs_out = np.empty_like(cs)
+        y = np.empty((M, H, D))
+        rc = self.lib.kda_oracle_layer_step(M, H, D, _ptr(S), _ptr(x), _ptr(w), _ptr(cs),
+                                            _ptr(cs_out), _ptr(f), _ptr(A_log), _ptr(dt_bias),
+                                            _ptr(beta_logit), int(kind), float(lower_bound),
+                                            float(scale), float(eps), _ptr(og), _ptr(nw),
+                                            float(norm_eps), _ptr(y))
+        if rc != 0:
+            raise RuntimeError(f"kda_oracle_layer_step failed ({rc})")
+        return S, cs_out, y
 
 
 _DEFAULT: Oracle | None = None

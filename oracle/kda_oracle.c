@@ -14,10 +14,13 @@
  *
  * Sources (web pages, cited by title and section):
  *  [DD]  "GLM-5.3 deep dive" (gangliao.me, 2026):
- *        8.2.2 (delta rule), 8.2.3 (KDA update, Eq. 1, and the order of
- *        operations in fla's reference recurrence), 8.2.4 (the full layer:
- *        short convolution with SiLU, split into heads, L2 normalisation),
- *        8.2.6 (decoding: fade, predict, correct, read; epsilon 1e-6, q scale).
+ *        8.2.2 (delta rule), 8.2.3 (KDA update, Eq. 1, the order of
+ *        operations in fla's reference recurrence, and the forget gate as
+ *        fla computes it), 8.2.4 (the full layer: short convolution with
+ *        SiLU, split into heads, write strength, forget gate, L2
+ *        normalisation, gated RMSNorm on the output; implementation notes:
+ *        FusedRMSNormGated(128, eps 1e-5, sigmoid)), 8.2.6 (decoding: fade,
+ *        predict, correct, read; epsilon 1e-6, q scale).
  *  [P1]  "At the 262k cap the DSA indexer costs 12x the sparse MLA it selects
  *        for", sections "Geometry" and "Bytes per stream" (depthwise conv,
  *        kernel 4, 3 cached taps, 3 tensors).
@@ -28,7 +31,9 @@
  *    multiplies the current token, tap 0 the oldest cached token; the cached
  *    taps are raw pre-conv inputs;
  *  - L2 norm: x * 1/sqrt(sum x^2 + eps);
- *  - the q scale is an argument (1/sqrt(D) in fla's decode, 1 in Eq. 1).
+ *  - the q scale is an argument (1/sqrt(D) in fla's decode, 1 in Eq. 1);
+ *  - gated RMSNorm: y = o / sqrt(mean(o^2) + eps) * w * sigmoid(g), per head
+ *    over its D outputs, from the unrounded o.
  */
 #include <math.h>
 #include <stddef.h>
@@ -38,7 +43,7 @@
 #include <omp.h>
 #endif
 
-int kda_oracle_version(void) { return 1; }
+int kda_oracle_version(void) { return 2; }
 
 int kda_oracle_max_threads(void)
 {
@@ -229,4 +234,132 @@ int kda_oracle_recurrent_step(int M, int H, int D, double *S,
         free(kh);
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gate, write strength and output norm around the recurrence.               */
+
+static double sigmoid_d(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* softplus(x) = log(1 + exp(x)), written so that exp never overflows:
+ * for x > 0, log(1 + e^x) = x + log(1 + e^-x). */
+static double softplus_d(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+/*
+ * Forget gate of one head, [DD] 8.2.3 "The gate in GLM-5.3-Flash, as fla
+ * computes it", for the D channels c of head h:
+ *
+ *   kind 0 (with a lower bound lb < 0, GLM-5.3-Flash: lb = -5):
+ *       g_c = lb * sigmoid(exp(A_h) * (f_c + b_c))
+ *   kind 1 (fla's default, no floor):
+ *       g_c = -exp(A_h) * softplus(f_c + b_c)
+ *   alpha_c = exp(g_c)
+ *
+ * f is the raw gate projection, A_h the head's A_log, b the head's dt_bias.
+ */
+void kda_oracle_gate(int D, const double *f, double A_log, const double *dt_bias,
+                     int kind, double lower_bound, double *alpha)
+{
+    const double eA = exp(A_log);
+    for (int c = 0; c < D; ++c) {
+        const double xin = f[c] + dt_bias[c];
+        const double g = kind == 0 ? lower_bound * sigmoid_d(eA * xin)
+                                   : -eA * softplus_d(xin);
+        alpha[c] = exp(g);
+    }
+}
+
+/* Write strength, [DD] 8.2.4 step 4: beta = sigmoid(logit), one per head. */
+void kda_oracle_beta(int n, const double *logit, double *beta)
+{
+    for (int i = 0; i < n; ++i)
+        beta[i] = sigmoid_d(logit[i]);
+}
+
+/*
+ * Gated RMSNorm of one head's outputs, [DD] 8.2.4 step 7 and implementation
+ * notes (FusedRMSNormGated over head_dim 128, eps 1e-5, sigmoid gate):
+ *
+ *   y_j = o_j / sqrt((1/D) sum_i o_i^2 + eps) * w_j * sigmoid(g_j)
+ */
+void kda_oracle_gated_rmsnorm(int D, const double *o, const double *g,
+                              const double *w, double eps, double *y)
+{
+    double ss = 0.0;
+    for (int i = 0; i < D; ++i)
+        ss += o[i] * o[i];
+    const double r = 1.0 / sqrt(ss / D + eps);
+    for (int j = 0; j < D; ++j)
+        y[j] = o[j] * r * w[j] * sigmoid_d(g[j]);
+}
+
+/*
+ * The decode step with its gate inputs in raw form ([DD] 8.2.4 steps 4 and
+ * 5): alpha from the forget gate of every (stream, head), beta from its
+ * logit, then kda_oracle_decode_step.
+ *
+ *   f       [M][H*D]  raw forget-gate projection
+ *   A_log   [H]       per head
+ *   dt_bias [H*D]     per head and channel
+ *   blogit  [M][H]    write-strength logits
+ */
+int kda_oracle_decode_step_gated(int M, int H, int D, double *S, const double *x,
+                                 const double *w, const double *cs_in,
+                                 double *cs_out, const double *f,
+                                 const double *A_log, const double *dt_bias,
+                                 const double *blogit, int kind,
+                                 double lower_bound, double scale, double eps,
+                                 double *o)
+{
+    if (M < 0 || H < 1 || D < 1)
+        return 1;
+    const size_t units = (size_t)M * H;
+    double *alpha = (double *)malloc(sizeof(double) * (units > 0 ? units : 1) * (size_t)D);
+    double *beta = (double *)malloc(sizeof(double) * (units > 0 ? units : 1));
+    if (!alpha || !beta) {
+        free(alpha);
+        free(beta);
+        return 2;
+    }
+    for (size_t u = 0; u < units; ++u) {
+        const size_t h = u % (size_t)H;
+        kda_oracle_gate(D, f + u * (size_t)D, A_log[h], dt_bias + h * (size_t)D, kind,
+                        lower_bound, alpha + u * (size_t)D);
+    }
+    kda_oracle_beta((int)units, blogit, beta);
+    int rc = kda_oracle_decode_step(M, H, D, S, x, w, cs_in, cs_out, alpha, beta, scale, eps, o);
+    free(alpha);
+    free(beta);
+    return rc;
+}
+
+/*
+ * The layer's recurrent core for one token: the gated decode step above,
+ * then the gated RMSNorm of every head's outputs ([DD] 8.2.4 steps 2-7 up
+ * to the final projection).
+ *
+ *   og      [M][H*D]  output-gate projection
+ *   norm_w  [D]       RMSNorm weight, shared by the heads
+ *   y       [M][H][D] output
+ */
+int kda_oracle_layer_step(int M, int H, int D, double *S, const double *x,
+                          const double *w, const double *cs_in, double *cs_out,
+                          const double *f, const double *A_log,
+                          const double *dt_bias, const double *blogit, int kind,
+                          double lower_bound, double scale, double eps,
+                          const double *og, const double *norm_w, double norm_eps,
+                          double *y)
+{
+    const size_t units = (size_t)(M > 0 ? M : 0) * (size_t)(H > 0 ? H : 0);
+    double *o = (double *)malloc(sizeof(double) * (units > 0 ? units : 1) * (size_t)(D > 0 ? D : 1));
+    if (!o)
+        return 2;
+    int rc = kda_oracle_decode_step_gated(M, H, D, S, x, w, cs_in, cs_out, f, A_log, dt_bias,
+                                          blogit, kind, lower_bound, scale, eps, o);
+    if (rc == 0)
+        for (size_t u = 0; u < units; ++u)
+            kda_oracle_gated_rmsnorm(D, o + u * (size_t)D, og + u * (size_t)D, norm_w, norm_eps,
+                                     y + u * (size_t)D);
+    free(o);
+    return rc;
 }

@@ -9,7 +9,10 @@ the oracle disagrees with something it must reproduce:
 * library routines for the special cases that reduce to them
   (torch's depthwise conv1d, SiLU and normalize, in float64);
 * closed forms and invariants the pages state (exact recall, identity at
-  alpha = 1 and beta = 0, the Householder contraction).
+  alpha = 1 and beta = 0, the Householder contraction);
+* the forget-gate table the pages print (keep factor, half-life, sigmoid
+  output), torch's sigmoid and rms_norm for the write strength and the
+  gated output norm.
 
 ``test_oracle_pins.py`` runs them on the real oracle; ``test_oracle_mutants.py``
 plants mistakes in a copy of the oracle's C source and checks that every
@@ -386,6 +389,166 @@ def pin_unit_independence(orc, M=3, H=4, D=8, seed=23):
             assert np.array_equal(o1[m, h], o2[m, h]) == same, f"output unit ({m},{h})"
 
 
+# --------------------------------------------------------------------------
+# 5. Forget gate, write strength, gated RMSNorm ("GLM-5.3 deep dive" 8.2.3,
+#    8.2.4)
+# --------------------------------------------------------------------------
+def _read_gate_table():
+    rows, neutral = [], None
+    with open(os.path.join(GOLDEN, "gate_half_life.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tag, *vals = line.split()
+            if tag == "row":
+                rows.append((vals[0], vals[1], vals[2]))
+            elif tag == "neutral":
+                neutral = [float(v) for v in vals]
+    return rows, neutral
+
+
+def _logit(p):
+    return math.log(p) - math.log1p(-p)
+
+
+def pin_gate_table(orc):
+    """Every row of the pages' table, at A_h = 0 (Miles' initial value): the
+    sigmoid output s is produced by f + b = logit(s); the oracle's alpha must
+    round to the printed keep factor and its half-life to the printed one."""
+    rows, neutral = _read_gate_table()
+    assert len(rows) == 5 and neutral is not None
+    for alpha_txt, half_txt, s_txt in rows:
+        x = 50.0 if s_txt == "to1" else _logit(float(s_txt))
+        a = float(orc.gate(np.array([x]), 0.0, np.array([0.0]), kind=0, lower_bound=-5.0)[0])
+        digits = len(alpha_txt.split(".")[1])
+        assert round(a, digits) == float(alpha_txt), f"alpha {a} for s={s_txt}, printed {alpha_txt}"
+        half = math.log(0.5) / math.log(a)
+        if half_txt == "under1":
+            assert 0 < half < 1, f"half-life {half} for printed alpha {alpha_txt}"
+        else:
+            assert int(half) == int(half_txt), f"half-life {half} for printed {half_txt}"
+    A, fb, g, alpha = neutral
+    a = float(orc.gate(np.array([fb]), A, np.array([0.0]), kind=0, lower_bound=-5.0)[0])
+    assert abs(math.log(a) - g) < 1e-12 and round(a, 3) == alpha, f"neutral point {a}"
+    # the floor: alpha stays above exp(-5) for any input, and reaches it in the limit
+    big = orc.gate(np.array([-80.0, 0.0, 80.0]), 0.0, np.zeros(3))
+    assert np.all(big >= math.exp(-5.0)) and np.all(big <= 1.0)
+    assert abs(big[2] - math.exp(-5.0)) < 1e-15 and big[0] > 1.0 - 1e-15
+
+
+def pin_gate_structure(orc, seed=30):
+    """The gate reads f and dt_bias only through f + b: (f, b, A) and
+    (f - c, b + c, A) agree.  exp(A_h) scales the sigmoid's input in the
+    bounded form (A = ln 2 at x/2 equals A = 0 at x) and the log-decay in
+    the softplus form (A = ln 2 squares alpha).  Alpha falls as f + b grows."""
+    rng = np.random.default_rng(seed)
+    f = rng.standard_normal(16) * 3
+    b = rng.standard_normal(16)
+    c = rng.standard_normal(16)
+    for kind in (0, 1):
+        a1 = orc.gate(f, 0.3, b, kind=kind)
+        a2 = orc.gate(f - c, 0.3, b + c, kind=kind)
+        _close(a1, a2, 1e-14, f"gate kind {kind}: shift between f and dt_bias")
+        if kind == 0:      # exp(A) multiplies the sigmoid's input
+            a3 = orc.gate((f + b) / 2, math.log(2.0), np.zeros(16), kind=kind)
+            a4 = orc.gate(f + b, 0.0, np.zeros(16), kind=kind)
+        else:              # exp(A) multiplies the log-decay: alpha is raised to exp(A)
+            a3 = orc.gate(f + b, math.log(2.0), np.zeros(16), kind=kind)
+            a4 = orc.gate(f + b, 0.0, np.zeros(16), kind=kind) ** 2
+        _close(a3, a4, 1e-14, f"gate kind {kind}: how exp(A_log) enters")
+        xs = np.linspace(-6, 6, 25)
+        al = orc.gate(xs, 0.0, np.zeros(25), kind=kind)
+        assert np.all(np.diff(al) < 0) and np.all((al > 0) & (al < 1)), f"gate kind {kind} monotone in (0, 1)"
+
+
+def pin_gate_softplus_closed_form(orc, seed=31):
+    """fla's default gate exp(-exp(A) softplus(x)) is sigmoid(-x) ** exp(A);
+    at A = 0 it is the tiny workload's alpha = exp(-softplus(g)) = 1/(1+e^g)."""
+    rng = np.random.default_rng(seed)
+    xs = rng.standard_normal(20) * 4
+    for A in (0.0, -0.7, 1.3):
+        got = orc.gate(xs, A, np.zeros(20), kind=1)
+        want = np.array([(1.0 / (1.0 + math.exp(x))) ** math.exp(A) for x in xs])
+        _close(got, want, 1e-13, f"softplus gate at A={A}")
+    # no overflow far out: softplus(800) = 800
+    far = orc.gate(np.array([800.0, -800.0]), 0.0, np.zeros(2), kind=1)
+    assert far[0] == 0.0 and far[1] == 1.0
+
+
+def pin_beta_sigmoid(orc, seed=32):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal(50) * 5
+    got = orc.beta(z)
+    _close(got, torch.sigmoid(torch.tensor(z, dtype=torch.float64)).numpy(), 1e-15, "beta vs torch.sigmoid")
+    assert orc.beta(np.array([0.0]))[0] == 0.5
+    _close(orc.beta(z) + orc.beta(-z), np.ones(50), 1e-15, "sigmoid(x) + sigmoid(-x) = 1")
+
+
+def pin_gated_rmsnorm(orc, D=128, seed=33):
+    """torch's rms_norm (float64) times torch.sigmoid of the gate; a constant
+    vector normalises to c/sqrt(c^2 + eps); without eps the norm ignores the
+    scale of o and flips with its sign."""
+    rng = np.random.default_rng(seed)
+    o = rng.standard_normal(D) * 0.3
+    g = rng.standard_normal(D) * 2
+    w = 1.0 + 0.1 * rng.standard_normal(D)
+    ot, gt, wt = (torch.tensor(v, dtype=torch.float64) for v in (o, g, w))
+    want = (F.rms_norm(ot, (D,), weight=wt, eps=1e-5) * torch.sigmoid(gt)).numpy()
+    _close(orc.gated_rmsnorm(o, g, w, eps=1e-5), want, 1e-14, "gated rmsnorm vs torch")
+    c = 0.01
+    y = orc.gated_rmsnorm(np.full(D, c), np.zeros(D), np.ones(D), eps=1e-5)
+    _close(y, np.full(D, 0.5 * c / math.sqrt(c * c + 1e-5)), 1e-14, "constant vector")
+    y1 = orc.gated_rmsnorm(o, g, w, eps=0.0)
+    _close(orc.gated_rmsnorm(7.5 * o, g, w, eps=0.0), y1, 1e-14, "scale invariance")
+    _close(orc.gated_rmsnorm(-o, g, w, eps=0.0), -y1, 1e-14, "sign")
+
+
+def _gate_inputs(rng, M, H, D):
+    f = rng.standard_normal((M, H * D))
+    A = rng.uniform(-0.5, 0.5, H)
+    b = rng.normal(-4.0, 1.5, H * D)
+    bl = rng.standard_normal((M, H))
+    return f, A, b, bl
+
+
+def pin_gated_step_wiring(orc, M=2, H=3, D=8, seed=34):
+    """decode_step_gated = decode_step with alpha from each (stream, head)'s
+    own f, A_log[h], dt_bias[h] and beta = sigmoid(logit); layer_step = its
+    outputs through the gated RMSNorm of each head with out_gate of that
+    (stream, head).  Heads get distinct gate parameters so a wrong index shows."""
+    rng = np.random.default_rng(seed)
+    S = rng.standard_normal((M, H, D, D)) * 0.1
+    x = rng.standard_normal((M, 3, H * D))
+    w = rng.standard_normal((3 * H * D, 4)) * 0.5
+    cs = rng.standard_normal((M, 3, 3 * H * D))
+    f, A, b, bl = _gate_inputs(rng, M, H, D)
+    og = rng.standard_normal((M, H * D))
+    nw = 1.0 + 0.1 * rng.standard_normal(D)
+    for kind, lb in ((0, -5.0), (1, 0.0)):
+        alpha = np.empty((M, H, D))
+        for m in range(M):
+            for h in range(H):
+                fb = f[m, h * D:(h + 1) * D] + b[h * D:(h + 1) * D]
+                if kind == 0:
+                    g = lb / (1.0 + np.exp(-np.exp(A[h]) * fb))
+                else:
+                    g = -np.exp(A[h]) * np.log1p(np.exp(fb))
+                alpha[m, h] = np.exp(g)
+        beta = 1.0 / (1.0 + np.exp(-bl))
+        S1, cs1, o1 = orc.decode_step(S, x, w, cs, alpha, beta, 0.25)
+        S2, cs2, o2 = orc.decode_step_gated(S, x, w, cs, f, A, b, bl, 0.25, kind=kind, lower_bound=lb)
+        _close(S2, S1, 1e-13, f"gated step state, kind {kind}")
+        _close(o2, o1, 1e-13, f"gated step output, kind {kind}")
+        assert np.array_equal(cs1, cs2)
+        S3, cs3, y = orc.layer_step(S, x, w, cs, f, A, b, bl, 0.25, og, nw, kind=kind, lower_bound=lb)
+        _close(S3, S1, 1e-13, f"layer step state, kind {kind}")
+        ot = torch.tensor(o1.reshape(M * H, D), dtype=torch.float64)
+        gt = torch.tensor(og.reshape(M * H, D), dtype=torch.float64)
+        want = F.rms_norm(ot, (D,), weight=torch.tensor(nw, dtype=torch.float64), eps=1e-5) * torch.sigmoid(gt)
+        _close(y.reshape(M * H, D), want.numpy(), 1e-13, f"layer step output, kind {kind}")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_unrolled_product,
@@ -402,4 +565,10 @@ ALL_PINS = [
     pin_decode_step_end_to_end,
     pin_recurrent_matches_decode,
     pin_unit_independence,
+    pin_gate_table,
+    pin_gate_structure,
+    pin_gate_softplus_closed_form,
+    pin_beta_sigmoid,
+    pin_gated_rmsnorm,
+    pin_gated_step_wiring,
 ]

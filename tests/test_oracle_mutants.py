@@ -41,6 +41,25 @@ MUTANTS = {
                          "        kda_oracle_delta_step(D, D, S + u * (size_t)D * D, qh, kh, zv,\n"
                          "                              alpha + u * (size_t)D, beta[u], o + u * (size_t)D);\n"
                          "        free(qh);\n        free(kh);\n    }\n    free(z);")],
+    "gate_A_not_exponentiated": [("const double eA = exp(A_log);", "const double eA = A_log;")],
+    "gate_bias_subtracted": [("const double xin = f[c] + dt_bias[c];", "const double xin = f[c] - dt_bias[c];")],
+    "gate_bound_sign": [("g = kind == 0 ? lower_bound * sigmoid_d(eA * xin)",
+                         "g = kind == 0 ? -lower_bound * sigmoid_d(eA * xin)")],
+    "gate_log_space_alpha": [("alpha[c] = exp(g);", "alpha[c] = 1.0 + g;")],
+    "gate_softplus_as_relu": [("return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));",
+                               "return x > 0.0 ? x : 0.0;")],
+    "gate_sigmoid_of_raw": [("g = kind == 0 ? lower_bound * sigmoid_d(eA * xin)",
+                             "g = kind == 0 ? lower_bound * sigmoid_d(xin)")],
+    "gate_A_of_first_head": [("kda_oracle_gate(D, f + u * (size_t)D, A_log[h],",
+                              "kda_oracle_gate(D, f + u * (size_t)D, A_log[0],")],
+    "gate_bias_ignores_head": [("A_log[h], dt_bias + h * (size_t)D, kind,", "A_log[h], dt_bias, kind,")],
+    "beta_no_sigmoid": [("beta[i] = sigmoid_d(logit[i]);", "beta[i] = logit[i];")],
+    "rmsnorm_sum_not_mean": [("const double r = 1.0 / sqrt(ss / D + eps);", "const double r = 1.0 / sqrt(ss + eps);")],
+    "rmsnorm_no_gate": [("y[j] = o[j] * r * w[j] * sigmoid_d(g[j]);", "y[j] = o[j] * r * w[j];")],
+    "rmsnorm_swish_gate": [("y[j] = o[j] * r * w[j] * sigmoid_d(g[j]);",
+                            "y[j] = o[j] * r * w[j] * g[j] * sigmoid_d(g[j]);")],
+    "rmsnorm_no_weight": [("y[j] = o[j] * r * w[j] * sigmoid_d(g[j]);", "y[j] = o[j] * r * sigmoid_d(g[j]);")],
+    "layer_gate_of_other_head": [("og + u * (size_t)D, norm_w, norm_eps,", "og, norm_w, norm_eps,")],
 }
 
 
