@@ -36,10 +36,15 @@ TRAFFIC_FILE = os.path.join(PROFILES, "decode_kernel_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "hybrid_linear_attention_kda_amd", "csrc", "kda_kernels.hip")
 METRIC = "KDA decode state GB/s + ms/layer at M=8,32 (FP32/BF16 state), % HBM peak"
 
-# algorithmic bytes per (stream, layer) besides the state: x 49,152 + conv
-# state read and written 294,912 + alpha 32,768 + beta 256 + o 16,384
-SIDE_BYTES_PER_STREAM = 393_472
-CONV_W_BYTES_PER_LAYER = 196_608
+# algorithmic bytes besides the state, (per stream, per layer): the plain
+# step reads x 49,152, reads and writes the conv state 294,912, reads alpha
+# 32,768 and beta 256 and writes o 16,384 per stream; conv weights 196,608
+# per layer.  The gated step takes the raw gate instead of alpha and beta: x + conv state
+# + f 16,384 + beta logit 128 + o 16,384 per stream; dt_bias 32,768 and
+# A_log 256 per layer.  The layer step adds the output gate (16,384 per
+# stream) and the norm weight (512 per layer); y replaces o.
+SIDE_BYTES = {"plain": (393_472, 196_608), "gated": (376_960, 196_608 + 32_768 + 256),
+              "layer": (393_344, 196_608 + 32_768 + 256 + 512)}
 
 
 def log(msg):
@@ -54,7 +59,7 @@ def kernel_source_hash() -> str:
 class Model:
     """34 layers of device buffers plus pre-marshalled C-ABI arguments."""
 
-    def __init__(self, wl, state_dtype, n_inputs, device="cuda:0"):
+    def __init__(self, wl, state_dtype, n_inputs, device="cuda:0", mode="plain"):
         import torch
 
         import kda_synth
@@ -68,38 +73,54 @@ class Model:
             li = kda_synth.layer_inputs(wl, layer, device, state_dtype)
             o = torch.empty((M, H, D), dtype=torch.bfloat16, device=device)
             ins = [kda_synth.step_inputs(wl, layer, t, device) for t in range(n_inputs)]
-            self.layers.append({"state": li["state"], "conv_w": li["conv_w"],
-                                "conv": li["conv_state"], "o": o, "inputs": ins})
+            entry = {"state": li["state"], "conv_w": li["conv_w"], "conv": li["conv_state"],
+                     "o": o, "inputs": ins}
+            if mode != "plain":
+                entry["gp"] = kda_synth.gate_params(wl, layer, device)
+                entry["gi"] = [kda_synth.gate_inputs(wl, layer, t, device) for t in range(n_inputs)]
+            self.layers.append(entry)
         torch.cuda.synchronize()
         sdt = kda.KDA_STATE_F32 if state_dtype == "f32" else kda.KDA_STATE_BF16
         self.n_inputs = n_inputs
+        self.mode = mode
         self.args = []   # [input set][layer] -> tuple of C arguments (stream last)
         vp = ctypes.c_void_p
         for t in range(n_inputs):
             row = []
             for L in self.layers:
                 inp = L["inputs"][t]
-                row.append((M, H, D, sdt, vp(L["state"].data_ptr()), vp(inp["x"].data_ptr()),
-                            vp(L["conv_w"].data_ptr()), vp(L["conv"].data_ptr()),
-                            vp(L["conv"].data_ptr()), vp(inp["alpha"].data_ptr()),
-                            vp(inp["beta"].data_ptr()), ctypes.c_float(wl.scale),
-                            vp(L["o"].data_ptr())))
+                head = (M, H, D, sdt, vp(L["state"].data_ptr()), vp(inp["x"].data_ptr()),
+                        vp(L["conv_w"].data_ptr()), vp(L["conv"].data_ptr()), vp(L["conv"].data_ptr()))
+                if mode == "plain":
+                    row.append(head + (vp(inp["alpha"].data_ptr()), vp(inp["beta"].data_ptr()),
+                                       ctypes.c_float(wl.scale), vp(L["o"].data_ptr())))
+                    continue
+                gi, gp = L["gi"][t], L["gp"]
+                gated = head + (vp(gi["f"].data_ptr()), vp(gp["A_log"].data_ptr()),
+                                vp(gp["dt_bias"].data_ptr()), vp(gi["beta_logit"].data_ptr()),
+                                kda.KDA_GATE_BOUNDED, ctypes.c_float(-5.0), ctypes.c_float(wl.scale))
+                if mode == "gated":
+                    row.append(gated + (vp(L["o"].data_ptr()),))
+                else:
+                    row.append(gated + (vp(gi["out_gate"].data_ptr()), vp(gp["norm_w"].data_ptr()),
+                                        ctypes.c_float(1e-5), vp(L["o"].data_ptr())))
             self.args.append(row)
 
     def state_bytes_per_layer(self):
         return self.wl.state_bytes(self.state_dtype)
 
     def alg_bytes_per_launch(self):
-        return (self.state_bytes_per_layer() * 2 + self.wl.M * SIDE_BYTES_PER_STREAM
-                + CONV_W_BYTES_PER_LAYER)
+        per_stream, per_layer = SIDE_BYTES[self.mode]
+        return self.state_bytes_per_layer() * 2 + self.wl.M * per_stream + per_layer
 
     def step(self, t, stream_ptr):
-        fn = self.lib.kda_decode_step
+        fn = {"plain": self.lib.kda_decode_step, "gated": self.lib.kda_decode_step_gated,
+              "layer": self.lib.kda_decode_layer_step}[self.mode]
         s = ctypes.c_void_p(stream_ptr)
         for a in self.args[t % self.n_inputs]:
             rc = fn(*a, s)
             if rc:
-                raise RuntimeError(f"kda_decode_step returned {rc}")
+                raise RuntimeError(f"{self.mode} decode step returned {rc}")
 
 
 def time_model(model, steps, warmup, use_graph):
@@ -136,8 +157,8 @@ def time_model(model, steps, warmup, use_graph):
     return start.elapsed_time(end) / 1e3, ("hipGraph" if use_graph else "eager")
 
 
-def measure(wl, state_dtype, steps, warmup, n_inputs):
-    model = Model(wl, state_dtype, n_inputs)
+def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain"):
+    model = Model(wl, state_dtype, n_inputs, mode=mode)
     res = {}
     for use_graph in (False, True):
         sec, mode = time_model(model, steps, warmup, use_graph)
@@ -349,20 +370,25 @@ def main():
 
     secondary = []
     if not args.no_secondary:
-        for name, sdt in (("glm_m8", "f32"), ("glm_m8", "bf16"), ("glm_m128", "bf16"),
-                          ("glm_m1", "f32")):
+        for name, sdt, mode in (("glm_m8", "f32", "plain"), ("glm_m8", "bf16", "plain"),
+                                ("glm_m128", "bf16", "plain"), ("glm_m1", "f32", "plain"),
+                                ("glm_m32", "f32", "gated"), ("glm_m32", "f32", "layer")):
             w2 = kda_synth.WORKLOADS[name]
             if name == "glm_m1":
                 w2 = kda_synth.Workload(**{**w2.__dict__, "layers": 34, "name": "glm_m1_34"})
-            r = measure(w2, sdt, max(20, args.steps // 4), args.warmup, n_inputs=min(w2.steps, 8))
-            entry = {"workload": name, "M": w2.M, "layers": w2.layers, "state_dtype": sdt,
+            r = measure(w2, sdt, max(20, args.steps // 4), args.warmup, n_inputs=min(w2.steps, 8),
+                        mode=mode)
+            entry = {"workload": name if mode == "plain" else f"{name}_{mode}", "M": w2.M,
+                     "layers": w2.layers, "state_dtype": sdt, "entry_point": {
+                         "plain": "kda_decode_step", "gated": "kda_decode_step_gated",
+                         "layer": "kda_decode_layer_step"}[mode],
                      "launch": r["launch"], "ms_per_layer": r["ms_per_layer"],
                      "ms_per_34_layer_step": r["ms_per_step"], "state_GBps": r["state_GBps"],
                      "frac_hbm_peak_state": r["state_GBps"] / HBM_PEAK_GBS,
                      "modes": r["modes"]}
             secondary.append(entry)
-            log(f"  {name} {sdt}: {r['launch']} {r['ms_per_layer'] * 1e3:.2f} us/layer "
-                f"{r['state_GBps']:.0f} GB/s")
+            log(f"  {entry['workload']} {sdt}: {r['launch']} {r['ms_per_layer'] * 1e3:.2f} us/layer "
+                f"{r['state_GBps']:.0f} GB/s, algorithmic {r['modes'][r['launch']]['alg_GBps']:.0f} GB/s")
 
     ceiling = None
     if not args.no_ceiling:

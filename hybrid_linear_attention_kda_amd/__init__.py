@@ -6,11 +6,15 @@ and a thin ctypes binding (``kda.py``) with the same entry-point names.
 """
 from .kda import (  # noqa: F401
     EXPORTS,
+    KDA_GATE_BOUNDED,
+    KDA_GATE_SOFTPLUS,
     KDA_STATE_BF16,
     KDA_STATE_F32,
     KdaError,
     kda_conv_step,
+    kda_decode_layer_step,
     kda_decode_step,
+    kda_decode_step_gated,
     kda_recurrent_step,
     kda_status_string,
     kda_version,

@@ -63,6 +63,7 @@ int choose_split(int M, int H, int D, int sdt, bool conv_in_place) {
 
 struct StepSizes {
     size_t state, x, w, conv, alpha, beta, o, qkv;
+    size_t fgate, A_log, dt_bias, blogit, norm_w;
 };
 
 int step_sizes(int M, int H, int D, int sdt, StepSizes* s) {
@@ -76,6 +77,11 @@ int step_sizes(int M, int H, int D, int sdt, StepSizes* s) {
     if (!checked_bytes(M, H, 1, 1, 4, &s->beta)) return KDA_ERR_ARG;
     if (!checked_bytes(M, H, D, 1, 2, &s->o)) return KDA_ERR_ARG;
     if (!checked_bytes(M, 3, HD, 1, 4, &s->qkv)) return KDA_ERR_ARG;
+    if (!checked_bytes(M, H, D, 1, 2, &s->fgate)) return KDA_ERR_ARG;
+    if (!checked_bytes(1, H, 1, 1, 4, &s->A_log)) return KDA_ERR_ARG;
+    if (!checked_bytes(1, H, D, 1, 4, &s->dt_bias)) return KDA_ERR_ARG;
+    if (!checked_bytes(M, H, 1, 1, 2, &s->blogit)) return KDA_ERR_ARG;
+    if (!checked_bytes(1, D, 1, 1, 4, &s->norm_w)) return KDA_ERR_ARG;
     // the kernels index workgroups as M*H*nsplit in 32 bits
     if ((long long)M * H * 4 > 0x7fffffffLL) return KDA_ERR_ARG;
     return KDA_OK;
@@ -135,9 +141,98 @@ int run_decode(int M, int H, int D, int sdt, void* state, const void* x, const v
     return map_hip(kda::launch_decode_step(a));
 }
 
+// The gated step and the layer step: the inputs of kda_decode_step without
+// alpha and beta, plus the raw gate inputs (and, for the layer step, the
+// output gate and norm weight).  `out` is o or y.
+struct GatedCall {
+    int M, H, D, sdt;
+    void* state;
+    const void *x, *w, *cin;
+    void* cout;
+    const void* fgate;
+    const float *A_log, *dt_bias;
+    const void* blogit;
+    int gate_kind;
+    float lower_bound, scale;
+    const void* ogate;      // layer step only (else NULL)
+    const float* norm_w;    // layer step only
+    float norm_eps;
+    void* out;
+    void* stream;
+};
+
+int run_gated(const GatedCall& c, bool layer) {
+    int rc = check_common(c.M, c.H, c.D, c.sdt, c.scale);
+    if (rc != KDA_OK) return rc;
+    if (c.gate_kind != KDA_GATE_BOUNDED && c.gate_kind != KDA_GATE_SOFTPLUS) return KDA_ERR_ARG;
+    if (c.gate_kind == KDA_GATE_BOUNDED && !(isfinite(c.lower_bound) && c.lower_bound < 0.0f))
+        return KDA_ERR_ARG;
+    if (layer && !(isfinite(c.norm_eps) && c.norm_eps >= 0.0f)) return KDA_ERR_ARG;
+    if (c.M == 0) return KDA_OK;
+    const void* need[] = {c.state, c.x, c.w, c.cin, c.cout, c.fgate, c.A_log, c.dt_bias, c.blogit, c.out};
+    for (const void* p : need)
+        if (!p) return KDA_ERR_NULL;
+    if (layer && (!c.ogate || !c.norm_w)) return KDA_ERR_NULL;
+    for (const void* p : need)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    if (layer && (!aligned16(c.ogate) || !aligned16(c.norm_w))) return KDA_ERR_ALIGN;
+    StepSizes sz;
+    rc = step_sizes(c.M, c.H, c.D, c.sdt, &sz);
+    if (rc != KDA_OK) return rc;
+    const Range rs = span(c.state, sz.state), ro = span(c.out, sz.o), rco = span(c.cout, sz.conv);
+    Range inputs[9] = {span(c.x, sz.x), span(c.w, sz.w), span(c.cin, sz.conv),
+                       span(c.fgate, sz.fgate), span(c.A_log, sz.A_log), span(c.dt_bias, sz.dt_bias),
+                       span(c.blogit, sz.blogit), Range{0, 0}, Range{0, 0}};
+    int n_in = 7;
+    if (layer) {
+        inputs[n_in++] = span(c.ogate, sz.fgate);
+        inputs[n_in++] = span(c.norm_w, sz.norm_w);
+    }
+    for (int i = 0; i < n_in; ++i)
+        if (overlap(rs, inputs[i]) || overlap(ro, inputs[i])) return KDA_ERR_ALIAS;
+    if (overlap(rs, ro) || overlap(rs, rco) || overlap(ro, rco)) return KDA_ERR_ALIAS;
+    for (int i = 0; i < n_in; ++i) {
+        if (i == 2 && c.cout == c.cin) continue;  // exact in-place conv state is allowed
+        if (overlap(rco, inputs[i])) return KDA_ERR_ALIAS;
+    }
+    kda::StepArgs a{};
+    a.M = c.M; a.H = c.H; a.D = c.D; a.state_dtype = c.sdt;
+    a.nsplit = layer ? 1 : choose_split(c.M, c.H, c.D, c.sdt, c.cout == c.cin);
+    a.state = c.state; a.x = c.x; a.conv_w = c.w; a.conv_in = c.cin; a.conv_out = c.cout;
+    a.scale = c.scale; a.o = c.out; a.stream = c.stream;
+    a.fgate = c.fgate; a.A_log = c.A_log; a.dt_bias = c.dt_bias; a.beta_logit = c.blogit;
+    a.gate_kind = c.gate_kind; a.lower_bound = c.lower_bound;
+    a.out_gate = c.ogate; a.norm_w = c.norm_w; a.norm_eps = c.norm_eps;
+    return map_hip(layer ? kda::launch_layer_step(a) : kda::launch_decode_step_gated(a));
+}
+
 }  // namespace
 
 extern "C" {
+
+int kda_decode_step_gated(int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                          const void* conv_w, const void* conv_in, void* conv_out,
+                          const void* f_gate, const float* A_log, const float* dt_bias,
+                          const void* beta_logit, int gate_kind, float gate_lower_bound,
+                          float scale, void* o, void* stream) {
+    GatedCall c{M, H, D, state_dtype, state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log,
+                dt_bias, beta_logit, gate_kind, gate_lower_bound, scale, nullptr, nullptr, 0.0f,
+                o, stream};
+    return run_gated(c, false);
+}
+
+int kda_decode_layer_step(int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                          const void* conv_w, const void* conv_in, void* conv_out,
+                          const void* f_gate, const float* A_log, const float* dt_bias,
+                          const void* beta_logit, int gate_kind, float gate_lower_bound,
+                          float scale, const void* out_gate, const float* norm_weight,
+                          float norm_eps, void* y, void* stream) {
+    GatedCall c{M, H, D, state_dtype, state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log,
+                dt_bias, beta_logit, gate_kind, gate_lower_bound, scale, out_gate, norm_weight,
+                norm_eps, y, stream};
+    return run_gated(c, true);
+}
+
 
 int kda_decode_step(int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
                     const void* conv_w, const void* conv_in, void* conv_out, const float* alpha,
@@ -211,12 +306,12 @@ const char* kda_status_string(int status) {
     case KDA_ERR_DTYPE: return "unknown state dtype";
     case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KDA_ERR_ALIAS: return "an output overlaps an input";
-    case KDA_ERR_ARG: return "invalid argument (negative size, non-finite scale, overflow)";
+    case KDA_ERR_ARG: return "invalid argument (negative size, non-finite scale, bad gate or norm parameter, overflow)";
     case KDA_ERR_HIP: return "the HIP runtime refused the launch";
     default: return "unknown status";
     }
 }
 
-int kda_version(void) { return 10000; }
+int kda_version(void) { return 10100; }
 
 }  // extern "C"

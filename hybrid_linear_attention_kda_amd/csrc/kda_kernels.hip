@@ -176,6 +176,17 @@ struct Ptrs {
     const float* beta;
     float scale;
     uint16_t* o;
+    // gated prologue (MODE >= 1): raw gate inputs instead of alpha / beta
+    const uint16_t* fgate;     // bf16 [M][H*D] forget-gate projection
+    const float* A_log;        // [H]
+    const float* dt_bias;      // [H*D]
+    const uint16_t* blogit;    // bf16 [M][H] write-strength logits
+    int gate_kind;             // 0: bounded sigmoid, 1: softplus
+    float lower_bound;         // gate_kind 0 only
+    // gated RMSNorm epilogue (MODE == 2): o is replaced by y
+    const uint16_t* ogate;     // bf16 [M][H*D] output-gate projection
+    const float* norm_w;       // [D]
+    float norm_eps;
 };
 
 // Workgroup b -> (unit = m*H + h, split).  Plain: the splits of a unit are
@@ -219,8 +230,12 @@ struct Pro {
     u32x2 xv, t0, t1, t2;      // raw bf16 x and taps of 4 channels (FUSED)
     u32x4 w01, w23;            // their 4 conv taps each
     f32x4 q0;                  // f32 q|k|v of 4 channels (!FUSED)
-    f32x4 av;                  // 4 alpha values
-    float b;                   // beta of the unit
+    f32x4 av;                  // 4 alpha values (MODE 0)
+    u32x2 fv;                  // 4 raw bf16 gate values (MODE >= 1)
+    f32x4 bias;                // their dt_bias
+    float alog;                // A_log of the head
+    float b;                   // beta of the unit (MODE 0), its logit (MODE >= 1)
+    float og, nw;              // output gate and norm weight of column tid (MODE 2)
 };
 
 // LDS of one workgroup: conv outputs (q at [0, D), k at [D, 2D), this
@@ -237,7 +252,7 @@ struct Smem {
 
 // Issue the small loads of unit `unit`: lanes [0, NG) own 4 channels each
 // (q, k, this split's v); the last D/4 lanes of the workgroup load alpha.
-template <class G, int D, bool FUSED>
+template <class G, int D, bool FUSED, int MODE>
 __device__ __forceinline__ void load_pro(Pro& in, const Ptrs& p, int unit, int split) {
     const int tid = threadIdx.x;
     const int m = unit / p.H, h = unit - m * p.H;
@@ -258,8 +273,37 @@ __device__ __forceinline__ void load_pro(Pro& in, const Ptrs& p, int unit, int s
         }
     }
     const int ag = tid - (G::NT - D / 4);
-    if (ag >= 0) in.av = *reinterpret_cast<const f32x4*>(p.alpha + (size_t)unit * D + 4 * ag);
-    in.b = p.beta[unit];
+    if constexpr (MODE == 0) {
+        if (ag >= 0) in.av = *reinterpret_cast<const f32x4*>(p.alpha + (size_t)unit * D + 4 * ag);
+        in.b = p.beta[unit];
+    } else {
+        if (ag >= 0) {
+            in.fv = ld8(p.fgate + (size_t)unit * D + 4 * ag);
+            in.bias = *reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)h * D + 4 * ag);
+        }
+        in.alog = p.A_log[h];
+        in.b = bf16_lo(p.blogit[unit]);
+        if constexpr (MODE == 2) {
+            if (tid < D) {
+                in.og = bf16_lo(p.ogate[(size_t)unit * D + tid]);
+                in.nw = p.norm_w[tid];
+            }
+        }
+    }
+}
+
+// Forget gate of one channel, "GLM-5.3 deep dive" 8.2.3 (the gate as fla
+// computes it): g = lb * sigmoid(exp(A) (f + b)) with a lower bound lb < 0,
+// or g = -exp(A) softplus(f + b); alpha = exp(g).
+__device__ __forceinline__ float gate_alpha(float fb, float eA, int kind, float lb) {
+    float g;
+    if (kind == 0) {
+        g = lb / (1.0f + expf(-eA * fb));
+    } else {
+        const float sp = fb > 0.0f ? fb + log1pf(expf(-fb)) : log1pf(expf(fb));
+        g = -eA * sp;
+    }
+    return expf(g);
 }
 
 // Issue every state load of this lane for unit `unit`.  live == false issues
@@ -277,7 +321,7 @@ __device__ __forceinline__ void load_state(typename G::raw_t (&raw)[G::RPL], con
 
 // Conv + SiLU of one unit's channels into LDS and the conv state shift;
 // alpha into LDS.  The caller places a barrier after it.
-template <class G, int D, bool FUSED>
+template <class G, int D, bool FUSED, int MODE>
 __device__ __forceinline__ void conv_unit(const Pro& in, const Ptrs& p, int unit, int split, Smem<G, D>& sm) {
     constexpr int NT = G::NT;
     const int tid = threadIdx.x;
@@ -313,14 +357,25 @@ __device__ __forceinline__ void conv_unit(const Pro& in, const Ptrs& p, int unit
         reinterpret_cast<f32x4*>(sm.z)[tid] = z0;
     }
     const int ag = tid - (NT - D / 4);
-    if (ag >= 0) reinterpret_cast<f32x4*>(sm.a)[ag] = in.av;
+    if (ag >= 0) {
+        if constexpr (MODE == 0) {
+            reinterpret_cast<f32x4*>(sm.a)[ag] = in.av;
+        } else {
+            const float eA = expf(in.alog);
+            reinterpret_cast<f32x4*>(sm.a)[ag] =
+                f32x4{gate_alpha(bf16_lo(in.fv.x) + in.bias.x, eA, p.gate_kind, p.lower_bound),
+                      gate_alpha(bf16_hi(in.fv.x) + in.bias.y, eA, p.gate_kind, p.lower_bound),
+                      gate_alpha(bf16_lo(in.fv.y) + in.bias.z, eA, p.gate_kind, p.lower_bound),
+                      gate_alpha(bf16_hi(in.fv.y) + in.bias.w, eA, p.gate_kind, p.lower_bound)};
+        }
+    }
 }
 
 // The rest of one unit, after conv_unit and a barrier: norms, fade and both
 // reductions, one cross-wave exchange, delta correction, readout, rank-1
 // write and the stores.
-template <typename TS, class G, int D>
-__device__ __forceinline__ void update_unit(float b, typename G::raw_t (&raw)[G::RPL], const Ptrs& p,
+template <typename TS, class G, int D, int MODE>
+__device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&raw)[G::RPL], const Ptrs& p,
                                             int unit, int split, Smem<G, D>& sm) {
     constexpr int NT = G::NT, COLS = G::COLS, CG = G::CG, RPL = G::RPL, VEC = G::IO_VEC;
     constexpr int NWAVES = NT / 64;
@@ -330,6 +385,10 @@ __device__ __forceinline__ void update_unit(float b, typename G::raw_t (&raw)[G:
     float* const s_q = sm.z;
     float* const s_k = sm.z + D;
     float* const s_v = sm.z + 2 * D;
+
+    // beta, or (MODE >= 1) the sigmoid of its logit ("GLM-5.3 deep dive"
+    // 8.2.4 step 4)
+    const float b = MODE == 0 ? in.b : 1.0f / (1.0f + expf(-in.b));
 
     // ---- L2 norms and k^.q^ (every wave reduces the same D values) ----
     float sqq = 0.0f, skk = 0.0f, sqk = 0.0f;
@@ -406,11 +465,11 @@ __device__ __forceinline__ void update_unit(float b, typename G::raw_t (&raw)[G:
         lds_barrier();
 #pragma unroll
         for (int e = 0; e < VEC; ++e) d[e] = sm.d[cg * VEC + e];
-        if (tid < COLS) ou[tid] = (uint16_t)f32_to_bf16_rne(fmaf(sm.d[tid], kq, sm.w[tid]));
+        if (MODE != 2 && tid < COLS) ou[tid] = (uint16_t)f32_to_bf16_rne(fmaf(sm.d[tid], kq, sm.w[tid]));
     } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) d[e] = b * (s_v[cg * VEC + e] - u[e]);
-        if (rw == 0) {
+        if (MODE != 2 && rw == 0) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 ou[cg * VEC + e] = (uint16_t)f32_to_bf16_rne(fmaf(d[e], kq, wq[e]));
@@ -425,12 +484,45 @@ __device__ __forceinline__ void update_unit(float b, typename G::raw_t (&raw)[G:
         for (int e = 0; e < VEC; ++e) sreg[t][e] = fmaf(kk[t], d[e], sreg[t][e]);
         G::IO::store(st + (size_t)G::row(wv, rw, t) * D + col0, sreg[t]);
     }
+
+    // ---- gated RMSNorm of the head's outputs (MODE 2), "GLM-5.3 deep dive"
+    // 8.2.4 step 7: y = o / sqrt(mean(o^2) + eps) * w * sigmoid(g), from the
+    // unrounded o; the state stores above are already in flight ----
+    if constexpr (MODE == 2) {
+        constexpr int HW = (D + 63) / 64;              // waves that hold one column each
+        static_assert(G::NSPLIT_ == 1 && HW <= NWAVES, "the output norm needs the whole head");
+        if constexpr (NWAVES == 1) {
+            // d and w are still per lane: put them in LDS like the
+            // cross-wave path does
+            if (rw == 0) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    sm.d[cg * VEC + e] = d[e];
+                    sm.w[cg * VEC + e] = wq[e];
+                }
+            }
+            lds_barrier();
+        }
+        float oj = 0.0f;
+        if (tid < D) oj = fmaf(sm.d[tid], kq, sm.w[tid]);
+        const float ss = wave_sum(oj * oj);
+        if (wv < HW && lane == 0) sm.red[wv][0][0] = ss;
+        lds_barrier();
+        if (tid < D) {
+            float tot = 0.0f;
+#pragma unroll
+            for (int w = 0; w < HW; ++w) tot += sm.red[w][0][0];
+            const float r = rsqrtf(tot / (float)D + p.norm_eps);
+            const float y = oj * r * in.nw / (1.0f + expf(-in.og));
+            ou[tid] = (uint16_t)f32_to_bf16_rne(y);
+        }
+    }
 }
 
 // One workgroup per (unit, split): grid M*H*NSPLIT.  The small prologue
 // loads go first, then every state load of the lane (all in flight
 // together); the conv + SiLU runs while the state is still arriving.
-template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG>
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG, int MODE>
 __global__ __launch_bounds__(NWAVES * 64)
 void decode_kernel(const Ptrs p, const int units)
 {
@@ -439,16 +531,16 @@ void decode_kernel(const Ptrs p, const int units)
     int unit, split;
     block_unit<NSPLIT, XG>((int)blockIdx.x, units, unit, split);
     Pro in;
-    load_pro<G, D, FUSED>(in, p, unit, split);
+    load_pro<G, D, FUSED, MODE>(in, p, unit, split);
     // keep the scheduler from sinking these loads below the state loads:
     // the conv prologue then waits only for them, not for the state
     __builtin_amdgcn_sched_barrier(0);
     typename G::raw_t raw[G::RPL];
     load_state<TS, G, D>(raw, p, unit, split, true);
     __builtin_amdgcn_sched_barrier(0);
-    conv_unit<G, D, FUSED>(in, p, unit, split, sm);
+    conv_unit<G, D, FUSED, MODE>(in, p, unit, split, sm);
     lds_barrier();
-    update_unit<TS, G, D>(in.b, raw, p, unit, split, sm);
+    update_unit<TS, G, D, MODE>(in, raw, p, unit, split, sm);
 }
 
 // -------------------------------------------------------------- conv step --
@@ -506,10 +598,19 @@ static Ptrs make_ptrs(const StepArgs& a) {
     p.beta = a.beta;
     p.scale = a.scale;
     p.o = static_cast<uint16_t*>(a.o);
+    p.fgate = static_cast<const uint16_t*>(a.fgate);
+    p.A_log = a.A_log;
+    p.dt_bias = a.dt_bias;
+    p.blogit = static_cast<const uint16_t*>(a.beta_logit);
+    p.gate_kind = a.gate_kind;
+    p.lower_bound = a.lower_bound;
+    p.ogate = static_cast<const uint16_t*>(a.out_gate);
+    p.norm_w = a.norm_w;
+    p.norm_eps = a.norm_eps;
     return p;
 }
 
-template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, bool FUSED, bool XG, int RMAP = 0>
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, bool FUSED, bool XG, int RMAP = 0, int MODE = 0>
 static hipError_t launch_decode(const StepArgs& a) {
     Ptrs p = make_ptrs(a);
     int units = a.M * a.H;
@@ -517,7 +618,7 @@ static hipError_t launch_decode(const StepArgs& a) {
     const dim3 grid((unsigned)((long)units * NSPLIT));
     const dim3 block(NWAVES * 64);
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&decode_kernel<TS, D, NSPLIT, NWAVES, VEC, RMAP, FUSED, XG>), grid,
+        reinterpret_cast<const void*>(&decode_kernel<TS, D, NSPLIT, NWAVES, VEC, RMAP, FUSED, XG, MODE>), grid,
         block, args, 0, (hipStream_t)a.stream);
 }
 
@@ -530,51 +631,54 @@ static hipError_t launch_decode(const StepArgs& a) {
 // A split leaves every workgroup a row segment of >= 128 bytes for f32 at
 // 2- and 4-way and bf16 at 2-way; bf16 at 4-way (64 bytes) is supported but
 // shares cache lines between workgroups and is never chosen by the library.
-template <bool FUSED>
+// The output norm (MODE 2) needs a whole head per workgroup: no splits.
+template <bool FUSED, int MODE>
 static hipError_t dispatch_wide_f32(const StepArgs& a) {
-    switch (a.nsplit) {
-    case 1:
-        return (long)a.M * a.H >= 2048 ? launch_decode<float, 128, 1, 16, 4, FUSED, false, 0>(a)
-                                       : launch_decode<float, 128, 1, 8, 4, FUSED, false, 0>(a);
-    case 2: return launch_decode<float, 128, 2, 8, 4, FUSED, true, 0>(a);
-    case 4: return launch_decode<float, 128, 4, 4, 4, FUSED, true, 0>(a);
-    default: return hipErrorInvalidValue;
+    if (a.nsplit == 1)
+        return (long)a.M * a.H >= 2048 ? launch_decode<float, 128, 1, 16, 4, FUSED, false, 0, MODE>(a)
+                                       : launch_decode<float, 128, 1, 8, 4, FUSED, false, 0, MODE>(a);
+    if constexpr (MODE != 2) {
+        if (a.nsplit == 2) return launch_decode<float, 128, 2, 8, 4, FUSED, true, 0, MODE>(a);
+        if (a.nsplit == 4) return launch_decode<float, 128, 4, 4, 4, FUSED, true, 0, MODE>(a);
     }
+    return hipErrorInvalidValue;
 }
 
-template <bool FUSED>
+template <bool FUSED, int MODE>
 static hipError_t dispatch_wide_bf16(const StepArgs& a) {
-    switch (a.nsplit) {
-    case 1: return launch_decode<uint16_t, 128, 1, 8, 8, FUSED, false, 1>(a);
-    case 2: return launch_decode<uint16_t, 128, 2, 4, 8, FUSED, true, 0>(a);
-    case 4: return launch_decode<uint16_t, 128, 4, 4, 8, FUSED, true, 0>(a);
-    default: return hipErrorInvalidValue;
+    if (a.nsplit == 1) return launch_decode<uint16_t, 128, 1, 8, 8, FUSED, false, 1, MODE>(a);
+    if constexpr (MODE != 2) {
+        if (a.nsplit == 2) return launch_decode<uint16_t, 128, 2, 4, 8, FUSED, true, 0, MODE>(a);
+        if (a.nsplit == 4) return launch_decode<uint16_t, 128, 4, 4, 8, FUSED, true, 0, MODE>(a);
     }
+    return hipErrorInvalidValue;
 }
 
-template <bool FUSED>
+template <bool FUSED, int MODE>
 static hipError_t dispatch(const StepArgs& a) {
     const bool f32 = a.state_dtype == 0;
     if (a.D != 128 && a.nsplit != 1) return hipErrorInvalidValue;
     switch (a.D) {
     case 16:
-        return f32 ? launch_decode<float, 16, 1, 1, 4, FUSED, false>(a)
-                   : launch_decode<uint16_t, 16, 1, 1, 4, FUSED, false>(a);
+        return f32 ? launch_decode<float, 16, 1, 1, 4, FUSED, false, 0, MODE>(a)
+                   : launch_decode<uint16_t, 16, 1, 1, 4, FUSED, false, 0, MODE>(a);
     case 32:
-        return f32 ? launch_decode<float, 32, 1, 1, 4, FUSED, false>(a)
-                   : launch_decode<uint16_t, 32, 1, 1, 8, FUSED, false>(a);
+        return f32 ? launch_decode<float, 32, 1, 1, 4, FUSED, false, 0, MODE>(a)
+                   : launch_decode<uint16_t, 32, 1, 1, 8, FUSED, false, 0, MODE>(a);
     case 64:
-        return f32 ? launch_decode<float, 64, 1, 2, 4, FUSED, false>(a)
-                   : launch_decode<uint16_t, 64, 1, 2, 8, FUSED, false>(a);
+        return f32 ? launch_decode<float, 64, 1, 2, 4, FUSED, false, 0, MODE>(a)
+                   : launch_decode<uint16_t, 64, 1, 2, 8, FUSED, false, 0, MODE>(a);
     case 128:
-        return f32 ? dispatch_wide_f32<FUSED>(a) : dispatch_wide_bf16<FUSED>(a);
+        return f32 ? dispatch_wide_f32<FUSED, MODE>(a) : dispatch_wide_bf16<FUSED, MODE>(a);
     default:
         return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_decode_step(const StepArgs& a) { return dispatch<true>(a); }
-hipError_t launch_recurrent_step(const StepArgs& a) { return dispatch<false>(a); }
+hipError_t launch_decode_step(const StepArgs& a) { return dispatch<true, 0>(a); }
+hipError_t launch_recurrent_step(const StepArgs& a) { return dispatch<false, 0>(a); }
+hipError_t launch_decode_step_gated(const StepArgs& a) { return dispatch<true, 1>(a); }
+hipError_t launch_layer_step(const StepArgs& a) { return dispatch<true, 2>(a); }
 
 hipError_t launch_conv_step(int M, int C, const void* x, const void* w, const void* cin,
                             void* cout, float* y, void* stream) {

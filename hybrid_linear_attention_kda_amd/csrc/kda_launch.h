@@ -20,12 +20,25 @@ struct StepArgs {
     const float* alpha;
     const float* beta;
     float scale;
-    void* o;
+    void* o;              // bf16 [M][H][D]: o, or y for the layer step
     void* stream;
+    // gated step and layer step
+    const void* fgate;       // bf16 [M][H*D]
+    const float* A_log;      // [H]
+    const float* dt_bias;    // [H*D]
+    const void* beta_logit;  // bf16 [M][H]
+    int gate_kind;
+    float lower_bound;
+    // layer step
+    const void* out_gate;    // bf16 [M][H*D]
+    const float* norm_w;     // [D]
+    float norm_eps;
 };
 
 hipError_t launch_decode_step(const StepArgs& a);
 hipError_t launch_recurrent_step(const StepArgs& a);
+hipError_t launch_decode_step_gated(const StepArgs& a);
+hipError_t launch_layer_step(const StepArgs& a);
 hipError_t launch_conv_step(int M, int C, const void* x, const void* w, const void* cin,
                             void* cout, float* y, void* stream);
 

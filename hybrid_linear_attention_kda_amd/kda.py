@@ -20,10 +20,12 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE = 0, 1, 2, 3
 KDA_ERR_ALIGN, KDA_ERR_ALIAS, KDA_ERR_ARG, KDA_ERR_HIP = 4, 5, 6, 7
 KDA_STATE_F32, KDA_STATE_BF16 = 0, 1
+KDA_GATE_BOUNDED, KDA_GATE_SOFTPLUS = 0, 1
 
 #: every symbol ``include/kda.h`` declares
-EXPORTS = ("kda_decode_step", "kda_decode_step_split", "kda_conv_step",
-           "kda_recurrent_step", "kda_status_string", "kda_version")
+EXPORTS = ("kda_decode_step", "kda_decode_step_split", "kda_decode_step_gated",
+           "kda_decode_layer_step", "kda_conv_step", "kda_recurrent_step",
+           "kda_status_string", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -49,6 +51,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_step.restype = i
     lib.kda_decode_step_split.argtypes = step + [i]
     lib.kda_decode_step_split.restype = i
+    gated = [i, i, i, i, vp, vp, vp, vp, vp, vp, fp, fp, vp, i, f, f]
+    lib.kda_decode_step_gated.argtypes = gated + [vp, vp]
+    lib.kda_decode_step_gated.restype = i
+    lib.kda_decode_layer_step.argtypes = gated + [vp, fp, f, vp, vp]
+    lib.kda_decode_layer_step.restype = i
     lib.kda_conv_step.argtypes = [i, i, vp, vp, vp, vp, fp, vp]
     lib.kda_conv_step.restype = i
     lib.kda_recurrent_step.argtypes = [i, i, i, i, vp, fp, fp, fp, f, vp, vp]
@@ -180,3 +187,56 @@ def kda_recurrent_step(state, qkv, alpha, beta, scale, o, stream=None):
     _check("kda_recurrent_step",
            lib.kda_recurrent_step(M, H, D, _state_code(state), _p(state), _p(qkv), _p(alpha),
                                   _p(beta), float(scale), _p(o), _stream(dev, stream)))
+
+
+def _gated_args(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt_bias, beta_logit,
+                gate_kind, lower_bound, scale):
+    if state.dim() != 4:
+        raise ValueError("state must be [M, H, D, D]")
+    M, H, D, _ = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("state must be a GPU tensor")
+    _need(state, "state", (M, H, D, D), state.dtype, dev)
+    _need(x_qkv, "x_qkv", (M, 3, H * D), torch.bfloat16, dev)
+    _need(conv_w, "conv_w", (3 * H * D, 4), torch.bfloat16, dev)
+    _need(conv_in, "conv_in", (M, 3, 3 * H * D), torch.bfloat16, dev)
+    _need(conv_out, "conv_out", (M, 3, 3 * H * D), torch.bfloat16, dev)
+    _need(f_gate, "f_gate", (M, H * D), torch.bfloat16, dev)
+    _need(A_log, "A_log", (H,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * D,), torch.float32, dev)
+    _need(beta_logit, "beta_logit", (M, H), torch.bfloat16, dev)
+    return (M, H, D, dev), (M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w),
+                            _p(conv_in), _p(conv_out), _p(f_gate), _p(A_log), _p(dt_bias),
+                            _p(beta_logit), int(gate_kind), float(lower_bound), float(scale))
+
+
+def kda_decode_step_gated(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt_bias,
+                          beta_logit, scale, o, gate_kind=KDA_GATE_BOUNDED, lower_bound=-5.0,
+                          stream=None):
+    """Fused step with raw gate inputs (see ``kda_decode_step_gated`` in kda.h):
+    f_gate [M,H*D] bf16, A_log [H] f32, dt_bias [H*D] f32, beta_logit [M,H]
+    bf16; o [M,H,D] bf16; the rest as kda_decode_step."""
+    lib = load()
+    (M, H, D, dev), args = _gated_args(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log,
+                                       dt_bias, beta_logit, gate_kind, lower_bound, scale)
+    _need(o, "o", (M, H, D), torch.bfloat16, dev)
+    _check("kda_decode_step_gated", lib.kda_decode_step_gated(*args, _p(o), _stream(dev, stream)))
+
+
+def kda_decode_layer_step(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt_bias,
+                          beta_logit, scale, out_gate, norm_weight, y,
+                          gate_kind=KDA_GATE_BOUNDED, lower_bound=-5.0, norm_eps=1e-5,
+                          stream=None):
+    """The gated step followed by the gated RMSNorm of every head (see
+    ``kda_decode_layer_step`` in kda.h): out_gate [M,H*D] bf16, norm_weight
+    [D] f32, y [M,H,D] bf16."""
+    lib = load()
+    (M, H, D, dev), args = _gated_args(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log,
+                                       dt_bias, beta_logit, gate_kind, lower_bound, scale)
+    _need(out_gate, "out_gate", (M, H * D), torch.bfloat16, dev)
+    _need(norm_weight, "norm_weight", (D,), torch.float32, dev)
+    _need(y, "y", (M, H, D), torch.bfloat16, dev)
+    _check("kda_decode_layer_step",
+           lib.kda_decode_layer_step(*args, _p(out_gate), _p(norm_weight), float(norm_eps), _p(y),
+                                     _stream(dev, stream)))

@@ -54,6 +54,14 @@ enum {
 /* Storage type of the recurrent state.  Arithmetic is f32 either way. */
 typedef enum { KDA_STATE_F32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype;
 
+/* Forget-gate forms ("GLM-5.3 deep dive", 8.2.3, the gate as fla computes
+ * it), per head h and key channel c, from the raw gate projection f:
+ *   KDA_GATE_BOUNDED:  g = lower_bound * sigmoid(exp(A_log[h]) * (f + dt_bias))
+ *                      (GLM-5.3-Flash: lower_bound = -5, so alpha > e^-5)
+ *   KDA_GATE_SOFTPLUS: g = -exp(A_log[h]) * softplus(f + dt_bias)  (fla's default)
+ *   alpha = exp(g). */
+typedef enum { KDA_GATE_BOUNDED = 0, KDA_GATE_SOFTPLUS = 1 } kda_gate_kind;
+
 /* epsilon inside the L2 norm: x * 1/sqrt(sum x^2 + eps) */
 #define KDA_L2NORM_EPS 1e-6f
 
@@ -108,6 +116,60 @@ int kda_decode_step_split(int M, int H, int D, int state_dtype,
                           const void *conv_in, void *conv_out,
                           const float *alpha, const float *beta, float scale,
                           void *o, void *stream, int nsplit);
+
+/*
+ * kda_decode_step_gated -- kda_decode_step with the step's gate inputs in
+ * raw form, computed in the kernel's prologue ("GLM-5.3 deep dive", 8.2.4
+ * steps 4 and 5; 8.2.3 for the gate): alpha from the forget gate, beta =
+ * sigmoid(beta_logit).  In place of alpha and beta it takes
+ *
+ *  f_gate      [M][H*D]  bf16: raw forget-gate projection of this token.
+ *  A_log       [H]       f32: per-head A_log.
+ *  dt_bias     [H*D]     f32: per-head, per-channel bias (shared by streams).
+ *  beta_logit  [M][H]    bf16: write-strength logits.
+ *  gate_kind   a kda_gate_kind; gate_lower_bound must be finite and < 0 for
+ *              KDA_GATE_BOUNDED and is ignored for KDA_GATE_SOFTPLUS.
+ *
+ * Everything else, the splits the library may choose, and the aliasing rules
+ * (the new inputs count as inputs) are those of kda_decode_step.  alpha and
+ * beta are formed in f32 and never written to memory.  Returns a KDA_*
+ * status (KDA_ERR_ARG for a bad gate_kind or lower bound).
+ */
+int kda_decode_step_gated(int M, int H, int D, int state_dtype,
+                          void *state, const void *x_qkv, const void *conv_w,
+                          const void *conv_in, void *conv_out,
+                          const void *f_gate, const float *A_log,
+                          const float *dt_bias, const void *beta_logit,
+                          int gate_kind, float gate_lower_bound, float scale,
+                          void *o, void *stream);
+
+/*
+ * kda_decode_layer_step -- the KDA layer's core for one token, between the
+ * input projections and the output projection ("GLM-5.3 deep dive", 8.2.4
+ * steps 2-7): kda_decode_step_gated followed by the gated RMSNorm of each
+ * head's outputs (8.2.4 step 7 and implementation notes:
+ * FusedRMSNormGated over the head's D outputs, sigmoid gate):
+ *
+ *   y_j = o_j / sqrt((1/D) sum_i o_i^2 + norm_eps) * norm_weight[j] * sigmoid(out_gate_j)
+ *
+ * computed from the unrounded f32 o (o itself is not written).
+ *
+ *  out_gate     [M][H*D]  bf16: output-gate projection of this token.
+ *  norm_weight  [D]       f32: RMSNorm weight, shared by the heads.
+ *  norm_eps     finite, >= 0 (1e-5 in GLM-5.3-Flash).
+ *  y            [M][H][D] bf16 output (rounded once, RNE).
+ *
+ * One workgroup always owns a whole head here (no column split).  Other
+ * arguments and rules as kda_decode_step_gated.  Returns a KDA_* status.
+ */
+int kda_decode_layer_step(int M, int H, int D, int state_dtype,
+                          void *state, const void *x_qkv, const void *conv_w,
+                          const void *conv_in, void *conv_out,
+                          const void *f_gate, const float *A_log,
+                          const float *dt_bias, const void *beta_logit,
+                          int gate_kind, float gate_lower_bound, float scale,
+                          const void *out_gate, const float *norm_weight,
+                          float norm_eps, void *y, void *stream);
 
 /*
  * kda_conv_step -- the conv stage alone, over C independent channels

@@ -24,6 +24,16 @@ the real dims; "N(0, s)" below means standard deviation s):
 * beta: sigmoid(N(0, 1)) per head in double, rounded to FP32; the
   serving-scale workload U(0, 1) with heads 0..4 of every stream pinned to
   0, 2^-24, 0.5, 1 - 2^-24 and 1.
+
+Raw gate inputs for the gated step and the layer step (trained values are
+not available; these put the keep factor mostly in (0.6, 0.99)):
+
+* A_log ~ U(-0.5, 0.5) per head and dt_bias ~ N(-4, 1) per channel, FP32,
+  fixed per layer;
+* forget-gate projection f ~ N(0, 1), BF16, per token;
+* write-strength logits ~ N(0, 1), BF16, per token;
+* output gate ~ N(0, 1), BF16, per token; RMSNorm weight 1 + 0.1 N(0, 1),
+  FP32, fixed per layer.
 """
 from __future__ import annotations
 
@@ -166,3 +176,22 @@ def custom(name: str, M: int, H: int, D: int, *, steps: int = 1, layers: int = 1
     return Workload(name, M=M, H=H, D=D, layers=layers, steps=steps,
                     state_dtypes=("f32", "bf16"), alpha_kind=alpha_kind,
                     beta_kind=beta_kind, conv_init=conv_init, seed=seed)
+
+
+def gate_params(wl: Workload, layer: int, device) -> dict:
+    """Per-layer gate and norm parameters: A_log [H], dt_bias [H*D], norm_w [D] (FP32)."""
+    H, D = wl.H, wl.D
+    ga = _gen(wl, layer, 0, "A_log", device)
+    A_log = (torch.rand((H,), generator=ga, device=device, dtype=torch.float64) - 0.5).to(F32)
+    dt_bias = (_randn((H * D,), _gen(wl, layer, 0, "dt_bias", device), device) - 4.0).to(F32)
+    norm_w = (1.0 + 0.1 * _randn((D,), _gen(wl, layer, 0, "norm_w", device), device)).to(F32)
+    return {"A_log": A_log, "dt_bias": dt_bias, "norm_w": norm_w}
+
+
+def gate_inputs(wl: Workload, layer: int, step: int, device) -> dict:
+    """Per-token raw gate inputs: f [M,H*D], beta_logit [M,H], out_gate [M,H*D], all BF16."""
+    M, H, D = wl.M, wl.H, wl.D
+    f = _randn((M, H * D), _gen(wl, layer, step, "f_gate", device), device).to(BF16)
+    bl = _randn((M, H), _gen(wl, layer, step, "beta_logit", device), device).to(BF16)
+    og = _randn((M, H * D), _gen(wl, layer, step, "out_gate", device), device).to(BF16)
+    return {"f": f, "beta_logit": bl, "out_gate": og}

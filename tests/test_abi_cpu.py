@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert kda.kda_version() == 10000
+    assert kda.kda_version() == 10100
     for code in range(8):
         s = kda.kda_status_string(code)
         assert s and s != "unknown status"
@@ -145,6 +145,72 @@ def test_recurrent_step_errors(lib):
         assert call(ptrs=q) == binding.KDA_ERR_ALIGN
     q = list(p); q[4] = q[0] + 64
     assert call(ptrs=q) == binding.KDA_ERR_ALIAS
+
+
+# ----------------------------------------------- gated step and layer step --
+# pointers: state, x, w, cin, cout, f, A_log, dt_bias, beta_logit, out[, out_gate, norm_w]
+def gated(lib, M=1, H=64, D=128, sdt=0, ptrs=None, kind=0, lb=-5.0, scale=0.125, layer=False,
+          norm_eps=1e-5, mis=None):
+    n = 12 if layer else 10
+    p = [fake(i) for i in range(n)] if ptrs is None else list(ptrs)
+    if mis is not None:
+        p[mis] += 8
+    head = (M, H, D, sdt, *p[:9], kind, lb, scale)
+    if layer:
+        return lib.kda_decode_layer_step(*head, p[10], p[11], norm_eps, p[9], None)
+    return lib.kda_decode_step_gated(*head, p[9], None)
+
+
+@pytest.mark.parametrize("layer", [False, True], ids=["gated", "layer"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), binding.KDA_ERR_ARG),
+    (dict(D=48), binding.KDA_ERR_SHAPE),
+    (dict(sdt=3), binding.KDA_ERR_DTYPE),
+    (dict(scale=math.nan), binding.KDA_ERR_ARG),
+    (dict(kind=2), binding.KDA_ERR_ARG),
+    (dict(kind=-1), binding.KDA_ERR_ARG),
+    (dict(kind=0, lb=0.0), binding.KDA_ERR_ARG),
+    (dict(kind=0, lb=1.0), binding.KDA_ERR_ARG),
+    (dict(kind=0, lb=math.nan), binding.KDA_ERR_ARG),
+    (dict(kind=0, lb=-math.inf), binding.KDA_ERR_ARG),
+])
+def test_gated_argument_errors(lib, kw, code, layer):
+    assert gated(lib, layer=layer, **kw) == code
+
+
+@pytest.mark.parametrize("eps", [-1e-5, math.nan, math.inf])
+def test_layer_norm_eps_errors(lib, eps):
+    assert gated(lib, layer=True, norm_eps=eps) == binding.KDA_ERR_ARG
+
+
+@pytest.mark.parametrize("layer,which", [(False, i) for i in range(10)] + [(True, i) for i in range(12)])
+def test_gated_null_and_misaligned(lib, layer, which):
+    n = 12 if layer else 10
+    p = [fake(i) for i in range(n)]
+    p[which] = None
+    assert gated(lib, ptrs=p, layer=layer) == binding.KDA_ERR_NULL
+    assert gated(lib, layer=layer, mis=which) == binding.KDA_ERR_ALIGN
+
+
+def test_gated_empty_batch_touches_nothing(lib):
+    assert gated(lib, M=0, ptrs=[None] * 10) == binding.KDA_OK
+    assert gated(lib, M=0, ptrs=[None] * 12, layer=True) == binding.KDA_OK
+
+
+def test_gated_aliasing(lib):
+    base = [fake(i) for i in range(12)]
+    for layer in (False, True):
+        n = 12 if layer else 10
+        p = list(base[:n]); p[9] = p[5]            # output over f_gate
+        assert gated(lib, ptrs=p, layer=layer) == binding.KDA_ERR_ALIAS
+        p = list(base[:n]); p[7] = p[0] + 256      # dt_bias inside the state
+        assert gated(lib, ptrs=p, layer=layer) == binding.KDA_ERR_ALIAS
+        p = list(base[:n]); p[8] = p[4] + 64       # beta_logit inside conv_out
+        assert gated(lib, ptrs=p, layer=layer) == binding.KDA_ERR_ALIAS
+    p = list(base); p[9] = p[10]                   # y over out_gate
+    assert gated(lib, ptrs=p, layer=True) == binding.KDA_ERR_ALIAS
+    p = list(base); p[11] = p[0] + 512             # norm weight inside the state
+    assert gated(lib, ptrs=p, layer=True) == binding.KDA_ERR_ALIAS
 
 
 def test_binding_rejects_host_tensors():
