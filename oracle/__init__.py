@@ -45,7 +45,7 @@ _CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
 
 def build(source: str = SOURCE, output: str = LIBRARY) -> str:
     """Compile ``source`` into the shared library ``output`` with gcc."""
-    tmp = output + ".tmp"
+    tmp = f"{output}.tmp{os.getpid()}"      # per process: parallel test workers may build at once
     cmd = ["gcc", *_CFLAGS, source, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, output)
@@ -97,6 +97,8 @@ class Oracle:
         lib.kda_oracle_decode_step_gated.restype = i
         lib.kda_oracle_layer_step.argtypes = [i, i, i, p, p, p, p, p, p, p, p, p, i, d, d, d, p, p, d, p]
         lib.kda_oracle_layer_step.restype = i
+        lib.kda_oracle_decode_multi.argtypes = [i, i, i, i, p, p, p, p, p, p, p, d, d, p]
+        lib.kda_oracle_decode_multi.restype = i
         self.lib = lib
 
     def max_threads(self) -> int:
@@ -232,6 +234,26 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"kda_oracle_layer_step failed ({rc})")
         return S, cs_out, y
+
+
+    def decode_multi(self, S, x, w, cs, alpha, beta, scale, eps=L2NORM_EPS):
+        """T consecutive tokens per stream: x [M,T,3,H*D], alpha [M,T,H,D],
+        beta [M,T,H]; S, w, cs as decode_step.  Returns (S_new, cs_new,
+        o [M,T,H,D])."""
+        S = _f64(S).copy()
+        M, H, D, _ = S.shape
+        x, w, cs = _f64(x), _f64(w), _f64(cs)
+        alpha, beta = _f64(alpha), _f64(beta)
+        T = x.shape[1]
+        assert x.shape == (M, T, 3, H * D) and alpha.shape == (M, T, H, D) and beta.shape == (M, T, H)
+        cs_out = np.empty_like(cs)
+        o = np.empty((M, T, H, D))
+        rc = self.lib.kda_oracle_decode_multi(T, M, H, D, _ptr(S), _ptr(x), _ptr(w), _ptr(cs),
+                                              _ptr(cs_out), _ptr(alpha), _ptr(beta), float(scale),
+                                              float(eps), _ptr(o))
+        if rc != 0:
+            raise RuntimeError(f"kda_oracle_decode_multi failed ({rc})")
+        return S, cs_out, o
 
 
 _DEFAULT: Oracle | None = None

@@ -363,3 +363,47 @@ int kda_oracle_layer_step(int M, int H, int D, double *S, const double *x,
     free(o);
     return rc;
 }
+
+/*
+ * T consecutive tokens of M streams in one call, [DD] 8.2.6 (fla's decode
+ * mode loops over the tokens of an input of at most 64 tokens): token t of
+ * every stream goes through kda_oracle_decode_step with the state and conv
+ * state left by token t - 1.
+ *
+ *   x      [M][T][3][H*D]   alpha [M][T][H][D]   beta [M][T][H]
+ *   o      [M][T][H][D]     S, w, cs_in, cs_out as kda_oracle_decode_step
+ */
+int kda_oracle_decode_multi(int T, int M, int H, int D, double *S, const double *x,
+                            const double *w, const double *cs_in, double *cs_out,
+                            const double *alpha, const double *beta, double scale,
+                            double eps, double *o)
+{
+    if (T < 0 || M < 0 || H < 1 || D < 1)
+        return 1;
+    const size_t HD = (size_t)H * D, C = 3 * HD;
+    if (cs_out != cs_in)
+        memcpy(cs_out, cs_in, sizeof(double) * (size_t)M * 3 * C);
+    double *xt = (double *)malloc(sizeof(double) * C);
+    double *at = (double *)malloc(sizeof(double) * HD);
+    double *bt = (double *)malloc(sizeof(double) * (size_t)H);
+    double *ot = (double *)malloc(sizeof(double) * HD);
+    if (!xt || !at || !bt || !ot) {
+        free(xt); free(at); free(bt); free(ot);
+        return 2;
+    }
+    int rc = 0;
+    for (int m = 0; m < M && rc == 0; ++m) {
+        double *Sm = S + (size_t)m * H * D * D;
+        double *cm = cs_out + (size_t)m * 3 * C;
+        for (int t = 0; t < T && rc == 0; ++t) {
+            const size_t mt = (size_t)m * T + t;
+            memcpy(xt, x + mt * C, sizeof(double) * C);
+            memcpy(at, alpha + mt * HD, sizeof(double) * HD);
+            memcpy(bt, beta + mt * H, sizeof(double) * (size_t)H);
+            rc = kda_oracle_decode_step(1, H, D, Sm, xt, w, cm, cm, at, bt, scale, eps, ot);
+            memcpy(o + mt * HD, ot, sizeof(double) * HD);
+        }
+    }
+    free(xt); free(at); free(bt); free(ot);
+    return rc;
+}

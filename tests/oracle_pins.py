@@ -549,6 +549,43 @@ def pin_gated_step_wiring(orc, M=2, H=3, D=8, seed=34):
         _close(y.reshape(M * H, D), want.numpy(), 1e-13, f"layer step output, kind {kind}")
 
 
+# --------------------------------------------------------------------------
+# 6. T tokens per call ("GLM-5.3 deep dive" 8.2.6: fla's decode mode loops
+#    over the tokens of a short input)
+# --------------------------------------------------------------------------
+def pin_multi_token(orc, M=2, H=2, D=8, T=5, seed=40):
+    """decode_multi over T tokens equals T single steps (state, conv state and
+    every token's output), and its recurrence part equals the chunkwise
+    WY/UT form of the deep dive's 8.2.5 over the same T tokens."""
+    rng = np.random.default_rng(seed)
+    S0 = rng.standard_normal((M, H, D, D)) * 0.1
+    x = rng.standard_normal((M, T, 3, H * D))
+    w = rng.standard_normal((3 * H * D, 4)) * 0.5
+    cs0 = rng.standard_normal((M, 3, 3 * H * D))
+    alpha = rng.uniform(0.5, 1.0, (M, T, H, D))
+    beta = rng.uniform(0.0, 1.0, (M, T, H))
+    S1, cs1, o1 = orc.decode_multi(S0, x, w, cs0, alpha, beta, 0.3)
+    S, cs = S0, cs0
+    for t in range(T):
+        S, cs, o = orc.decode_step(S, x[:, t], w, cs, alpha[:, t], beta[:, t], 0.3)
+        _close(o1[:, t], o, 1e-14, f"token {t} output")
+    _close(S1, S, 1e-14, "state after T tokens")
+    assert np.array_equal(cs1, cs), "conv state after T tokens"
+    # the recurrence alone: q, k, v of one (stream, head) through the chunk form
+    m, h = 1, 1
+    cs_t = cs0[m]
+    Q, K, V = [], [], []
+    for t in range(T):
+        zz, cs_t = orc.conv_silu(x[m, t].reshape(-1), w, cs_t)
+        zz = zz.reshape(3, H, D)[:, h]
+        Q.append(orc.l2norm(zz[0], scale=0.3))
+        K.append(orc.l2norm(zz[1]))
+        V.append(zz[2])
+    Sc, Oc = _chunk_wy(S0[m, h], np.array(K), np.array(Q), np.array(V), alpha[m, :, h], beta[m, :, h])
+    _close(S1[m, h], Sc, 1e-12, "state vs chunk form")
+    _close(o1[m, :, h], Oc, 1e-12, "outputs vs chunk form")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_unrolled_product,
@@ -571,4 +608,5 @@ ALL_PINS = [
     pin_beta_sigmoid,
     pin_gated_rmsnorm,
     pin_gated_step_wiring,
+    pin_multi_token,
 ]

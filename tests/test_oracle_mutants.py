@@ -60,6 +60,10 @@ MUTANTS = {
                             "y[j] = o[j] * r * w[j] * g[j] * sigmoid_d(g[j]);")],
     "rmsnorm_no_weight": [("y[j] = o[j] * r * w[j] * sigmoid_d(g[j]);", "y[j] = o[j] * r * sigmoid_d(g[j]);")],
     "layer_gate_of_other_head": [("og + u * (size_t)D, norm_w, norm_eps,", "og, norm_w, norm_eps,")],
+    "multi_conv_state_not_carried": [("rc = kda_oracle_decode_step(1, H, D, Sm, xt, w, cm, cm, at, bt, scale, eps, ot);",
+                                      "rc = kda_oracle_decode_step(1, H, D, Sm, xt, w, cs_in + (size_t)m * 3 * C, cm, at, bt, scale, eps, ot);")],
+    "multi_alpha_of_first_token": [("memcpy(at, alpha + mt * HD, sizeof(double) * HD);",
+                                    "memcpy(at, alpha + (size_t)m * T * HD, sizeof(double) * HD);")],
 }
 
 
