@@ -45,6 +45,11 @@ METRIC = "KDA decode state GB/s + ms/layer at M=8,32 (FP32/BF16 state), % HBM pe
 # stream) and the norm weight (512 per layer); y replaces o.
 SIDE_BYTES = {"plain": (393_472, 196_608), "gated": (376_960, 196_608 + 32_768 + 256),
               "layer": (393_344, 196_608 + 32_768 + 256 + 512)}
+# T tokens per call: per stream and token x 49,152 + alpha 32,768 + beta 256
+# + o 16,384; the conv state 294,912 once per call
+MULTI_TOKEN_BYTES, MULTI_CALL_BYTES = 98_560, 294_912
+MULTI_T = 8
+CONV_W_BYTES = 196_608
 
 
 def log(msg):
@@ -59,7 +64,7 @@ def kernel_source_hash() -> str:
 class Model:
     """34 layers of device buffers plus pre-marshalled C-ABI arguments."""
 
-    def __init__(self, wl, state_dtype, n_inputs, device="cuda:0", mode="plain"):
+    def __init__(self, wl, state_dtype, n_inputs, device="cuda:0", mode="plain", T=1):
         import torch
 
         import kda_synth
@@ -72,7 +77,16 @@ class Model:
         for layer in range(wl.layers):
             li = kda_synth.layer_inputs(wl, layer, device, state_dtype)
             o = torch.empty((M, H, D), dtype=torch.bfloat16, device=device)
-            ins = [kda_synth.step_inputs(wl, layer, t, device) for t in range(n_inputs)]
+            if mode == "multi":
+                # input set t = tokens [t*T, (t+1)*T), stacked on a token axis
+                ins = []
+                for t in range(n_inputs):
+                    toks = [kda_synth.step_inputs(wl, layer, t * T + j, device) for j in range(T)]
+                    ins.append({k: torch.stack([tk[k] for tk in toks], 1).contiguous()
+                                for k in ("x", "alpha", "beta")})
+                o = torch.empty((M, T, H, D), dtype=torch.bfloat16, device=device)
+            else:
+                ins = [kda_synth.step_inputs(wl, layer, t, device) for t in range(n_inputs)]
             entry = {"state": li["state"], "conv_w": li["conv_w"], "conv": li["conv_state"],
                      "o": o, "inputs": ins}
             if mode != "plain":
@@ -82,7 +96,7 @@ class Model:
         torch.cuda.synchronize()
         sdt = kda.KDA_STATE_F32 if state_dtype == "f32" else kda.KDA_STATE_BF16
         self.n_inputs = n_inputs
-        self.mode = mode
+        self.mode, self.T = mode, T
         self.args = []   # [input set][layer] -> tuple of C arguments (stream last)
         vp = ctypes.c_void_p
         for t in range(n_inputs):
@@ -91,9 +105,10 @@ class Model:
                 inp = L["inputs"][t]
                 head = (M, H, D, sdt, vp(L["state"].data_ptr()), vp(inp["x"].data_ptr()),
                         vp(L["conv_w"].data_ptr()), vp(L["conv"].data_ptr()), vp(L["conv"].data_ptr()))
-                if mode == "plain":
-                    row.append(head + (vp(inp["alpha"].data_ptr()), vp(inp["beta"].data_ptr()),
-                                       ctypes.c_float(wl.scale), vp(L["o"].data_ptr())))
+                if mode in ("plain", "multi"):
+                    args = head + (vp(inp["alpha"].data_ptr()), vp(inp["beta"].data_ptr()),
+                                   ctypes.c_float(wl.scale), vp(L["o"].data_ptr()))
+                    row.append(args if mode == "plain" else (T,) + args)
                     continue
                 gi, gp = L["gi"][t], L["gp"]
                 gated = head + (vp(gi["f"].data_ptr()), vp(gp["A_log"].data_ptr()),
@@ -110,12 +125,15 @@ class Model:
         return self.wl.state_bytes(self.state_dtype)
 
     def alg_bytes_per_launch(self):
+        if self.mode == "multi":
+            return (self.state_bytes_per_layer() * 2 + CONV_W_BYTES
+                    + self.wl.M * (self.T * MULTI_TOKEN_BYTES + MULTI_CALL_BYTES))
         per_stream, per_layer = SIDE_BYTES[self.mode]
         return self.state_bytes_per_layer() * 2 + self.wl.M * per_stream + per_layer
 
     def step(self, t, stream_ptr):
         fn = {"plain": self.lib.kda_decode_step, "gated": self.lib.kda_decode_step_gated,
-              "layer": self.lib.kda_decode_layer_step}[self.mode]
+              "layer": self.lib.kda_decode_layer_step, "multi": self.lib.kda_decode_multi}[self.mode]
         s = ctypes.c_void_p(stream_ptr)
         for a in self.args[t % self.n_inputs]:
             rc = fn(*a, s)
@@ -157,8 +175,8 @@ def time_model(model, steps, warmup, use_graph):
     return start.elapsed_time(end) / 1e3, ("hipGraph" if use_graph else "eager")
 
 
-def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain"):
-    model = Model(wl, state_dtype, n_inputs, mode=mode)
+def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain", T=1):
+    model = Model(wl, state_dtype, n_inputs, mode=mode, T=T)
     res = {}
     for use_graph in (False, True):
         sec, mode = time_model(model, steps, warmup, use_graph)
@@ -372,22 +390,28 @@ def main():
     if not args.no_secondary:
         for name, sdt, mode in (("glm_m8", "f32", "plain"), ("glm_m8", "bf16", "plain"),
                                 ("glm_m128", "bf16", "plain"), ("glm_m1", "f32", "plain"),
-                                ("glm_m32", "f32", "gated"), ("glm_m32", "f32", "layer")):
+                                ("glm_m32", "f32", "gated"), ("glm_m32", "f32", "layer"),
+                                ("glm_m32", "f32", "multi"), ("glm_m128", "bf16", "multi")):
             w2 = kda_synth.WORKLOADS[name]
             if name == "glm_m1":
                 w2 = kda_synth.Workload(**{**w2.__dict__, "layers": 34, "name": "glm_m1_34"})
-            r = measure(w2, sdt, max(20, args.steps // 4), args.warmup, n_inputs=min(w2.steps, 8),
-                        mode=mode)
+            T = MULTI_T if mode == "multi" else 1
+            r = measure(w2, sdt, max(20, args.steps // 4), args.warmup,
+                        n_inputs=1 if mode == "multi" else min(w2.steps, 8), mode=mode, T=T)
             entry = {"workload": name if mode == "plain" else f"{name}_{mode}", "M": w2.M,
-                     "layers": w2.layers, "state_dtype": sdt, "entry_point": {
-                         "plain": "kda_decode_step", "gated": "kda_decode_step_gated",
-                         "layer": "kda_decode_layer_step"}[mode],
+                     "layers": w2.layers, "state_dtype": sdt, "tokens_per_call": T,
+                     "entry_point": {"plain": "kda_decode_step", "gated": "kda_decode_step_gated",
+                                     "layer": "kda_decode_layer_step",
+                                     "multi": "kda_decode_multi"}[mode],
                      "launch": r["launch"], "ms_per_layer": r["ms_per_layer"],
                      "ms_per_34_layer_step": r["ms_per_step"], "state_GBps": r["state_GBps"],
                      "frac_hbm_peak_state": r["state_GBps"] / HBM_PEAK_GBS,
                      "modes": r["modes"]}
+            if mode == "multi":
+                entry["us_per_token_layer"] = r["ms_per_layer"] * 1e3 / T
+                entry["alg_GBps"] = r["modes"][r["launch"]]["alg_GBps"]
             secondary.append(entry)
-            log(f"  {entry['workload']} {sdt}: {r['launch']} {r['ms_per_layer'] * 1e3:.2f} us/layer "
+            log(f"  {entry['workload']} {sdt} T={T}: {r['launch']} {r['ms_per_layer'] * 1e3:.2f} us/call "
                 f"{r['state_GBps']:.0f} GB/s, algorithmic {r['modes'][r['launch']]['alg_GBps']:.0f} GB/s")
 
     ceiling = None

@@ -13,6 +13,7 @@ from .kda import (  # noqa: F401
     KdaError,
     kda_conv_step,
     kda_decode_layer_step,
+    kda_decode_multi,
     kda_decode_step,
     kda_decode_step_gated,
     kda_recurrent_step,

@@ -250,6 +250,45 @@ int kda_decode_step_split(int M, int H, int D, int state_dtype, void* state, con
                       scale, o, stream, nsplit);
 }
 
+int kda_decode_multi(int T, int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                     const void* conv_w, const void* conv_in, void* conv_out, const float* alpha,
+                     const float* beta, float scale, void* o, void* stream) {
+    if (T < 0) return KDA_ERR_ARG;
+    int rc = check_common(M, H, D, state_dtype, scale);
+    if (rc != KDA_OK) return rc;
+    if (M == 0 || T == 0) return KDA_OK;
+    const void* need[] = {state, x_qkv, conv_w, conv_in, conv_out, alpha, beta, o};
+    for (const void* p : need)
+        if (!p) return KDA_ERR_NULL;
+    for (const void* p : need)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    StepSizes sz;
+    rc = step_sizes(M, H, D, state_dtype, &sz);
+    if (rc != KDA_OK) return rc;
+    // per-token tensors span T times their single-token size
+    size_t bx, ba, bb, bo;
+    const long HD = (long)H * D;
+    if (!checked_bytes((long)M * T, 3, HD, 1, 2, &bx) || !checked_bytes((long)M * T, H, D, 1, 4, &ba) ||
+        !checked_bytes((long)M * T, H, 1, 1, 4, &bb) || !checked_bytes((long)M * T, H, D, 1, 2, &bo))
+        return KDA_ERR_ARG;
+    if ((long long)M * T * 3 * HD > 0x7fffffffLL * 4LL) return KDA_ERR_ARG;
+    const Range rs = span(state, sz.state), ro = span(o, bo), rco = span(conv_out, sz.conv);
+    const Range inputs[] = {span(x_qkv, bx), span(conv_w, sz.w), span(conv_in, sz.conv),
+                            span(alpha, ba), span(beta, bb)};
+    for (const Range& r : inputs)
+        if (overlap(rs, r) || overlap(ro, r)) return KDA_ERR_ALIAS;
+    if (overlap(rs, ro) || overlap(rs, rco) || overlap(ro, rco)) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i) {
+        if (i == 2 && conv_out == conv_in) continue;
+        if (overlap(rco, inputs[i])) return KDA_ERR_ALIAS;
+    }
+    kda::StepArgs a{};
+    a.M = M; a.H = H; a.D = D; a.T = T; a.state_dtype = state_dtype; a.nsplit = 1;
+    a.state = state; a.x = x_qkv; a.conv_w = conv_w; a.conv_in = conv_in; a.conv_out = conv_out;
+    a.alpha = alpha; a.beta = beta; a.scale = scale; a.o = o; a.stream = stream;
+    return map_hip(kda::launch_decode_multi(a));
+}
+
 int kda_conv_step(int M, int C, const void* x, const void* conv_w, const void* conv_in,
                   void* conv_out, float* y, void* stream) {
     if (M < 0 || C < 1 || (C % 8) != 0) return KDA_ERR_ARG;

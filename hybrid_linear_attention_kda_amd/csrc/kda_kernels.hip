@@ -543,6 +543,210 @@ void decode_kernel(const Ptrs p, const int units)
     update_unit<TS, G, D, MODE>(in, raw, p, unit, split, sm);
 }
 
+// ------------------------------------------------------- T tokens per launch --
+//
+// fla's decode mode runs inputs of up to 64 tokens through the recurrent form
+// ("GLM-5.3 deep dive" 8.2.6): here one workgroup owns one head for all T
+// tokens of a stream, so the state is read once and written once per launch
+// instead of once per token.  Per token: conv + SiLU (the taps shift in
+// registers), norms, fade, both reductions, delta correction, readout, and
+// the rank-1 write into the registers that hold the state.  The next token's
+// small inputs are loaded while the current token is computed.
+
+// The lane's inputs of one token: x of its 4 channels, 4 alpha values, beta.
+struct TokIn {
+    u32x2 x;
+    f32x4 a;
+    float b;
+};
+
+template <class G, int D>
+__device__ __forceinline__ void load_token(TokIn& in, const Ptrs& p, int T, int m, int h, size_t ch, int t) {
+    const int tid = threadIdx.x;
+    const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
+    const size_t mt = (size_t)m * T + t;
+    if (tid < G::NG) in.x = ld8(p.x + mt * C3 + ch);
+    const int ag = tid - (G::NT - D / 4);
+    if (ag >= 0) in.a = *reinterpret_cast<const f32x4*>(p.alpha + mt * HD + (size_t)h * D + 4 * ag);
+    in.b = p.beta[mt * p.H + h];
+}
+
+// One token of the multi-token kernel, from its conv to the rank-1 write.
+// FIRST: the state arrives in raw form (loaded before the first token) and
+// is unpacked here, after the first conv, so the conv does not wait for it.
+template <typename TS, class G, int D, bool FIRST>
+__device__ __forceinline__ void token_step(const TokIn& in, u32x2& t0, u32x2& t1, u32x2& t2,
+                                           const u32x4& w01, const u32x4& w23,
+                                           typename G::raw_t (&raw)[G::RPL], float (&sreg)[G::RPL][G::IO_VEC],
+                                           const Ptrs& p, int T, int m, int h, int t, Smem<G, D>& sm) {
+    constexpr int NT = G::NT, COLS = G::COLS, CG = G::CG, RPL = G::RPL, VEC = G::IO_VEC;
+    constexpr int NWAVES = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int cg = lane % CG, rw = lane / CG;
+    float* const s_q = sm.z;
+    float* const s_k = sm.z + D;
+    float* const s_v = sm.z + 2 * D;
+
+    if (tid < G::NG) {
+        reinterpret_cast<f32x4*>(sm.z)[tid] =
+            f32x4{conv_silu(u32x2{w01.x, w01.y}, bf16_lo(t0.x), bf16_lo(t1.x), bf16_lo(t2.x), bf16_lo(in.x.x)),
+                  conv_silu(u32x2{w01.z, w01.w}, bf16_hi(t0.x), bf16_hi(t1.x), bf16_hi(t2.x), bf16_hi(in.x.x)),
+                  conv_silu(u32x2{w23.x, w23.y}, bf16_lo(t0.y), bf16_lo(t1.y), bf16_lo(t2.y), bf16_lo(in.x.y)),
+                  conv_silu(u32x2{w23.z, w23.w}, bf16_hi(t0.y), bf16_hi(t1.y), bf16_hi(t2.y), bf16_hi(in.x.y))};
+        t0 = t1;
+        t1 = t2;
+        t2 = in.x;
+    }
+    const int ag = tid - (NT - D / 4);
+    if (ag >= 0) reinterpret_cast<f32x4*>(sm.a)[ag] = in.a;
+    lds_barrier();
+    if constexpr (FIRST) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) G::IO::unpack(raw[r], sreg[r]);
+    }
+
+    float sqq = 0.0f, skk = 0.0f, sqk = 0.0f;
+#pragma unroll
+    for (int i = lane; i < D; i += 64) {
+        const float qv = s_q[i], kv = s_k[i];
+        sqq = fmaf(qv, qv, sqq);
+        skk = fmaf(kv, kv, skk);
+        sqk = fmaf(qv, kv, sqk);
+    }
+    sqq = wave_sum(sqq);
+    skk = wave_sum(skk);
+    sqk = wave_sum(sqk);
+    const float rq = p.scale * rsqrtf(sqq + 1e-6f);
+    const float rk = rsqrtf(skk + 1e-6f);
+    const float kq = sqk * rq * rk;
+
+    float kk[RPL], u[VEC], wq[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) { u[e] = 0.0f; wq[e] = 0.0f; }
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int i = G::row(wv, rw, r);
+        const float a = sm.a[i], qq = s_q[i] * rq;
+        kk[r] = s_k[i] * rk;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float sv = sreg[r][e] * a;
+            sreg[r][e] = sv;
+            u[e] = fmaf(sv, kk[r], u[e]);
+            wq[e] = fmaf(sv, qq, wq[e]);
+        }
+    }
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            u[e] += __shfl_xor(u[e], off, 64);
+            wq[e] += __shfl_xor(wq[e], off, 64);
+        }
+    }
+
+    float d[VEC];
+    uint16_t* const ou = p.o + ((size_t)m * T + t) * ((size_t)p.H * D) + (size_t)h * D;
+    if constexpr (NWAVES > 1) {
+        static_assert(2 * COLS <= NT, "u and w sums need 2*COLS threads");
+        if (rw == 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                sm.red[wv][0][cg * VEC + e] = u[e];
+                sm.red[wv][1][cg * VEC + e] = wq[e];
+            }
+        }
+        lds_barrier();
+        if (tid < COLS) {
+            float U = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) U += sm.red[w][0][tid];
+            sm.d[tid] = in.b * (s_v[tid] - U);
+        } else if (tid < 2 * COLS) {
+            float W = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) W += sm.red[w][1][tid - COLS];
+            sm.w[tid - COLS] = W;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d[e] = sm.d[cg * VEC + e];
+        if (tid < COLS) ou[tid] = (uint16_t)f32_to_bf16_rne(fmaf(sm.d[tid], kq, sm.w[tid]));
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d[e] = in.b * (s_v[cg * VEC + e] - u[e]);
+        if (rw == 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                ou[cg * VEC + e] = (uint16_t)f32_to_bf16_rne(fmaf(d[e], kq, wq[e]));
+        }
+        // the next token overwrites the vectors this one read
+        lds_barrier();
+    }
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sreg[r][e] = fmaf(kk[r], d[e], sreg[r][e]);
+}
+
+// One workgroup per (stream, head), T >= 1 tokens; x [M][T][3][H*D],
+// alpha [M][T][H][D], beta [M][T][H], o [M][T][H][D].
+template <typename TS, int D, int NWAVES, int VEC, int RMAP>
+__global__ __launch_bounds__(NWAVES * 64)
+void decode_multi_kernel(const Ptrs p, const int units, const int T)
+{
+    typedef Geo<TS, D, 1, NWAVES, VEC, RMAP> G;
+    __shared__ Smem<G, D> sm;
+    const int unit = (int)blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int cg = lane % G::CG, rw = lane / G::CG;
+    const int m = unit / p.H, h = unit - m * p.H;
+    const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
+    const size_t ch = tid < G::NG ? group_channel<G, D>(tid, h, 0, HD) : 0;
+
+    u32x2 t0, t1, t2;
+    u32x4 w01, w23;
+    if (tid < G::NG) {
+        const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
+        t0 = ld8(ci);
+        t1 = ld8(ci + C3);
+        t2 = ld8(ci + 2 * C3);
+        const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
+        w01 = wp[0];
+        w23 = wp[1];
+    }
+    TokIn cur, nxt;
+    load_token<G, D>(cur, p, T, m, h, ch, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    TS* const st = static_cast<TS*>(p.state) + (size_t)unit * D * D + cg * G::IO_VEC;
+    typename G::raw_t raw[G::RPL];
+#pragma unroll
+    for (int r = 0; r < G::RPL; ++r) raw[r] = G::IO::load(st + (size_t)G::row(wv, rw, r) * D);
+    __builtin_amdgcn_sched_barrier(0);
+    float sreg[G::RPL][G::IO_VEC];
+
+    // token 0, then the rest; the next token's loads go out first (the last
+    // token re-reads its own inputs: a placeholder in bounds)
+    load_token<G, D>(nxt, p, T, m, h, ch, T > 1 ? 1 : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    token_step<TS, G, D, true>(cur, t0, t1, t2, w01, w23, raw, sreg, p, T, m, h, 0, sm);
+    for (int t = 1; t < T; ++t) {
+        cur = nxt;
+        load_token<G, D>(nxt, p, T, m, h, ch, t + 1 < T ? t + 1 : t);
+        __builtin_amdgcn_sched_barrier(0);
+        token_step<TS, G, D, false>(cur, t0, t1, t2, w01, w23, raw, sreg, p, T, m, h, t, sm);
+    }
+
+#pragma unroll
+    for (int r = 0; r < G::RPL; ++r) G::IO::store(st + (size_t)G::row(wv, rw, r) * D, sreg[r]);
+    if (tid < G::NG) {
+        uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + ch;
+        st8(co, t0);
+        st8(co + C3, t1);
+        st8(co + 2 * C3, t2);
+    }
+}
+
 // -------------------------------------------------------------- conv step --
 // One thread per 8 consecutive channels of one stream.
 __global__ __launch_bounds__(256)
@@ -672,6 +876,32 @@ static hipError_t dispatch(const StepArgs& a) {
         return f32 ? dispatch_wide_f32<FUSED, MODE>(a) : dispatch_wide_bf16<FUSED, MODE>(a);
     default:
         return hipErrorInvalidValue;
+    }
+}
+
+template <typename TS, int D, int NWAVES, int VEC, int RMAP>
+static hipError_t launch_multi(const StepArgs& a) {
+    Ptrs p = make_ptrs(a);
+    int units = a.M * a.H;
+    int T = a.T;
+    void* args[] = {(void*)&p, (void*)&units, (void*)&T};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_multi_kernel<TS, D, NWAVES, VEC, RMAP>),
+                           dim3((unsigned)units), dim3(NWAVES * 64), args, 0, (hipStream_t)a.stream);
+}
+
+// T tokens per launch: the whole-head shapes of the single-token step.
+hipError_t launch_decode_multi(const StepArgs& a) {
+    const bool f32 = a.state_dtype == 0;
+    switch (a.D) {
+    case 16: return f32 ? launch_multi<float, 16, 1, 4, 0>(a) : launch_multi<uint16_t, 16, 1, 4, 0>(a);
+    case 32: return f32 ? launch_multi<float, 32, 1, 4, 0>(a) : launch_multi<uint16_t, 32, 1, 8, 0>(a);
+    case 64: return f32 ? launch_multi<float, 64, 2, 4, 0>(a) : launch_multi<uint16_t, 64, 2, 8, 0>(a);
+    case 128:
+        if (f32)
+            return (long)a.M * a.H >= 2048 ? launch_multi<float, 128, 16, 4, 0>(a)
+                                           : launch_multi<float, 128, 8, 4, 0>(a);
+        return launch_multi<uint16_t, 128, 8, 8, 1>(a);
+    default: return hipErrorInvalidValue;
     }
 }
 

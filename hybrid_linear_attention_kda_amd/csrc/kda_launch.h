@@ -9,6 +9,7 @@ namespace kda {
 // Arguments of one decode / recurrent launch, already validated by the host.
 struct StepArgs {
     int M, H, D;
+    int T;                // tokens per stream (multi-token step)
     int state_dtype;      // 0 = f32, 1 = bf16
     int nsplit;           // workgroups per head: 1, 2 or 4 (D == 128 only)
     void* state;
@@ -39,6 +40,7 @@ hipError_t launch_decode_step(const StepArgs& a);
 hipError_t launch_recurrent_step(const StepArgs& a);
 hipError_t launch_decode_step_gated(const StepArgs& a);
 hipError_t launch_layer_step(const StepArgs& a);
+hipError_t launch_decode_multi(const StepArgs& a);
 hipError_t launch_conv_step(int M, int C, const void* x, const void* w, const void* cin,
                             void* cout, float* y, void* stream);
 

@@ -24,7 +24,7 @@ KDA_GATE_BOUNDED, KDA_GATE_SOFTPLUS = 0, 1
 
 #: every symbol ``include/kda.h`` declares
 EXPORTS = ("kda_decode_step", "kda_decode_step_split", "kda_decode_step_gated",
-           "kda_decode_layer_step", "kda_conv_step", "kda_recurrent_step",
+           "kda_decode_layer_step", "kda_decode_multi", "kda_conv_step", "kda_recurrent_step",
            "kda_status_string", "kda_version")
 
 
@@ -56,6 +56,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_step_gated.restype = i
     lib.kda_decode_layer_step.argtypes = gated + [vp, fp, f, vp, vp]
     lib.kda_decode_layer_step.restype = i
+    lib.kda_decode_multi.argtypes = [i] + step
+    lib.kda_decode_multi.restype = i
     lib.kda_conv_step.argtypes = [i, i, vp, vp, vp, vp, fp, vp]
     lib.kda_conv_step.restype = i
     lib.kda_recurrent_step.argtypes = [i, i, i, i, vp, fp, fp, fp, f, vp, vp]
@@ -240,3 +242,29 @@ def kda_decode_layer_step(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log
     _check("kda_decode_layer_step",
            lib.kda_decode_layer_step(*args, _p(out_gate), _p(norm_weight), float(norm_eps), _p(y),
                                      _stream(dev, stream)))
+
+
+def kda_decode_multi(state, x_qkv, conv_w, conv_in, conv_out, alpha, beta, scale, o, stream=None):
+    """T tokens per stream in one call (see ``kda_decode_multi`` in kda.h):
+    x_qkv [M,T,3,H*D] bf16, alpha [M,T,H,D] f32, beta [M,T,H] f32,
+    o [M,T,H,D] bf16; state, conv_w, conv_in/conv_out as kda_decode_step."""
+    lib = load()
+    if state.dim() != 4 or x_qkv.dim() != 4:
+        raise ValueError("state must be [M, H, D, D] and x_qkv [M, T, 3, H*D]")
+    M, H, D, _ = state.shape
+    T = x_qkv.shape[1]
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("state must be a GPU tensor")
+    _need(state, "state", (M, H, D, D), state.dtype, dev)
+    _need(x_qkv, "x_qkv", (M, T, 3, H * D), torch.bfloat16, dev)
+    _need(conv_w, "conv_w", (3 * H * D, 4), torch.bfloat16, dev)
+    _need(conv_in, "conv_in", (M, 3, 3 * H * D), torch.bfloat16, dev)
+    _need(conv_out, "conv_out", (M, 3, 3 * H * D), torch.bfloat16, dev)
+    _need(alpha, "alpha", (M, T, H, D), torch.float32, dev)
+    _need(beta, "beta", (M, T, H), torch.float32, dev)
+    _need(o, "o", (M, T, H, D), torch.bfloat16, dev)
+    _check("kda_decode_multi",
+           lib.kda_decode_multi(T, M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w),
+                                _p(conv_in), _p(conv_out), _p(alpha), _p(beta), float(scale), _p(o),
+                                _stream(dev, stream)))

@@ -172,6 +172,32 @@ int kda_decode_layer_step(int M, int H, int D, int state_dtype,
                           float norm_eps, void *y, void *stream);
 
 /*
+ * kda_decode_multi -- T consecutive tokens of each of M streams in one call
+ * (fla's decode mode runs inputs of up to 64 tokens through the recurrent
+ * form, "GLM-5.3 deep dive" 8.2.6): token t of a stream is the step of
+ * kda_decode_step applied to the state and conv state left by token t - 1.
+ * One workgroup keeps a head's state on chip for all T tokens, so the state
+ * is read and written once per call instead of once per token (with bf16
+ * storage it is also rounded once per call).  For speculative/MTP
+ * verification and short prefill.
+ *
+ *  T       tokens per stream, >= 0 (T == 0 or M == 0: nothing is touched).
+ *  x_qkv   [M][T][3][H*D]  bf16 pre-conv q|k|v of each token.
+ *  alpha   [M][T][H][D]    f32.
+ *  beta    [M][T][H]       f32.
+ *  o       [M][T][H][D]    bf16 output of every token.
+ *  state, conv_w, conv_in, conv_out, scale as kda_decode_step (conv_out may
+ *  be conv_in; it receives the last three raw inputs after token T - 1).
+ *
+ * Aliasing rules as kda_decode_step.  Returns a KDA_* status.
+ */
+int kda_decode_multi(int T, int M, int H, int D, int state_dtype,
+                     void *state, const void *x_qkv, const void *conv_w,
+                     const void *conv_in, void *conv_out,
+                     const float *alpha, const float *beta, float scale,
+                     void *o, void *stream);
+
+/*
  * kda_conv_step -- the conv stage alone, over C independent channels
  * ("GLM-5.3 deep dive", 8.2.4 step 2; one launch over all q|k|v channels).
  *

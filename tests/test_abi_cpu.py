@@ -213,6 +213,35 @@ def test_gated_aliasing(lib):
     assert gated(lib, ptrs=p, layer=True) == binding.KDA_ERR_ALIAS
 
 
+# ------------------------------------------------------------ T tokens ----
+def test_multi_errors(lib):
+    p = [fake(i) for i in range(8)]   # state, x, w, cin, cout, alpha, beta, o
+
+    def call(T=4, M=1, H=64, D=128, sdt=0, ptrs=p, scale=0.125):
+        s, x, w, ci, co, a, b, o = ptrs
+        return lib.kda_decode_multi(T, M, H, D, sdt, s, x, w, ci, co, a, b, scale, o, None)
+    assert call(T=-1) == binding.KDA_ERR_ARG
+    assert call(M=-1) == binding.KDA_ERR_ARG
+    assert call(D=100) == binding.KDA_ERR_SHAPE
+    assert call(sdt=9) == binding.KDA_ERR_DTYPE
+    assert call(scale=math.inf) == binding.KDA_ERR_ARG
+    assert call(T=0, ptrs=[None] * 8) == binding.KDA_OK
+    assert call(M=0, ptrs=[None] * 8) == binding.KDA_OK
+    for i in range(8):
+        q = list(p); q[i] = None
+        assert call(ptrs=q) == binding.KDA_ERR_NULL
+        q = list(p); q[i] += 4
+        assert call(ptrs=q) == binding.KDA_ERR_ALIGN
+    q = list(p); q[7] = q[1] + 4096     # o over the tokens' x
+    assert call(ptrs=q) == binding.KDA_ERR_ALIAS
+    q = list(p); q[4] = q[5] + 16       # conv_out inside alpha
+    assert call(ptrs=q) == binding.KDA_ERR_ALIAS
+    # o of T tokens spans T times one token's output: alpha placed 64 KiB past
+    # o is inside it at T = 64
+    q = list(p); q[5] = q[7] + 64 * 1024
+    assert call(T=64, ptrs=q) == binding.KDA_ERR_ALIAS
+
+
 def test_binding_rejects_host_tensors():
     M, H, D = 1, 2, 16
     st = torch.zeros(M, H, D, D)
