@@ -548,77 +548,109 @@ void decode_kernel(const Ptrs p, const int units)
 // fla's decode mode runs inputs of up to 64 tokens through the recurrent form
 // ("GLM-5.3 deep dive" 8.2.6): here one workgroup owns one head for all T
 // tokens of a stream, so the state is read once and written once per launch
-// instead of once per token.  Per token: conv + SiLU (the taps shift in
-// registers), norms, fade, both reductions, delta correction, readout, and
-// the rank-1 write into the registers that hold the state.  The next token's
-// small inputs are loaded while the current token is computed.
+// instead of once per token.
+//
+// Only the fade, the reductions and the rank-1 write depend on the state.
+// Everything else (conv + SiLU, the norms, alpha, beta) is computed for a
+// chunk of TC tokens at once: lane (j, g) of the workgroup computes the 4
+// channels of group g for token j of the chunk, reading the three previous
+// raw inputs of those channels (from x, or from the conv state for the first
+// three tokens); one wave per token then forms its norms.  The serial loop
+// over the chunk's tokens then touches only LDS and the state registers, with
+// two barriers per token.
 
-// The lane's inputs of one token: x of its 4 channels, 4 alpha values, beta.
-struct TokIn {
-    u32x2 x;
-    f32x4 a;
-    float b;
+template <typename TS, int D, int NWAVES, int VEC, int RMAP, int TCMAX = 16>
+struct MultiGeo {
+    typedef Geo<TS, D, 1, NWAVES, VEC, RMAP> G;
+    static constexpr int NGT = 3 * D / 4;            // channel groups of one token
+    static constexpr int TC = G::NT / NGT < TCMAX ? G::NT / NGT : TCMAX;   // tokens per chunk
+    static_assert(TC >= 1, "one token's channel groups must fit the workgroup");
+    static constexpr int ZW = 3 * D;                 // conv outputs of one token: q, k, v
 };
 
-template <class G, int D>
-__device__ __forceinline__ void load_token(TokIn& in, const Ptrs& p, int T, int m, int h, size_t ch, int t) {
-    const int tid = threadIdx.x;
-    const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
-    const size_t mt = (size_t)m * T + t;
-    if (tid < G::NG) in.x = ld8(p.x + mt * C3 + ch);
-    const int ag = tid - (G::NT - D / 4);
-    if (ag >= 0) in.a = *reinterpret_cast<const f32x4*>(p.alpha + mt * HD + (size_t)h * D + 4 * ag);
-    in.b = p.beta[mt * p.H + h];
+template <class MG, int D>
+struct MultiSmem {
+    __attribute__((aligned(16))) float z[MG::TC][MG::ZW];
+    __attribute__((aligned(16))) float a[MG::TC][D];
+    float b[MG::TC], rq[MG::TC], rk[MG::TC], kq[MG::TC];
+    float red[MG::G::NT / 64][2][D];
+    float d[D];
+    float w[D];
+};
+
+// Raw input (4 bf16 channels at channel offset ch) at sequence position pos
+// of stream m: pos < 0 is a cached tap (tap 3 + pos of conv_in), pos >= 0 is
+// token pos of x.
+__device__ __forceinline__ u32x2 seq_input(const Ptrs& p, int T, int m, size_t C3, size_t ch, int pos) {
+    if (pos < 0) return ld8(p.conv_in + (size_t)m * 3 * C3 + (size_t)(3 + pos) * C3 + ch);
+    return ld8(p.x + ((size_t)m * T + pos) * C3 + ch);
 }
 
-// One token of the multi-token kernel, from its conv to the rank-1 write.
-// FIRST: the state arrives in raw form (loaded before the first token) and
-// is unpacked here, after the first conv, so the conv does not wait for it.
-template <typename TS, class G, int D, bool FIRST>
-__device__ __forceinline__ void token_step(const TokIn& in, u32x2& t0, u32x2& t1, u32x2& t2,
-                                           const u32x4& w01, const u32x4& w23,
-                                           typename G::raw_t (&raw)[G::RPL], float (&sreg)[G::RPL][G::IO_VEC],
-                                           const Ptrs& p, int T, int m, int h, int t, Smem<G, D>& sm) {
+// Conv, alpha, beta and norms of tokens [c0, c0 + n) into LDS.
+template <class MG, int D>
+__device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, int c0, int n,
+                                            MultiSmem<MG, D>& sm) {
+    typedef typename MG::G G;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
+    const int j = tid / MG::NGT, g = tid - j * MG::NGT;
+    if (j < n) {
+        const int tok = c0 + j;
+        const size_t ch = group_channel<G, D>(g, h, 0, HD);
+        const u32x2 xv = seq_input(p, T, m, C3, ch, tok);
+        const u32x2 t2 = seq_input(p, T, m, C3, ch, tok - 1);
+        const u32x2 t1 = seq_input(p, T, m, C3, ch, tok - 2);
+        const u32x2 t0 = seq_input(p, T, m, C3, ch, tok - 3);
+        const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
+        const u32x4 w01 = wp[0], w23 = wp[1];
+        const size_t mt = (size_t)m * T + tok;
+        f32x4 av;
+        if (g < D / 4) av = *reinterpret_cast<const f32x4*>(p.alpha + mt * HD + (size_t)h * D + 4 * g);
+        float bv = 0.0f;
+        if (g == 0) bv = p.beta[mt * p.H + h];
+        reinterpret_cast<f32x4*>(sm.z[j])[g] =
+            f32x4{conv_silu(u32x2{w01.x, w01.y}, bf16_lo(t0.x), bf16_lo(t1.x), bf16_lo(t2.x), bf16_lo(xv.x)),
+                  conv_silu(u32x2{w01.z, w01.w}, bf16_hi(t0.x), bf16_hi(t1.x), bf16_hi(t2.x), bf16_hi(xv.x)),
+                  conv_silu(u32x2{w23.x, w23.y}, bf16_lo(t0.y), bf16_lo(t1.y), bf16_lo(t2.y), bf16_lo(xv.y)),
+                  conv_silu(u32x2{w23.z, w23.w}, bf16_hi(t0.y), bf16_hi(t1.y), bf16_hi(t2.y), bf16_hi(xv.y))};
+        if (g < D / 4) reinterpret_cast<f32x4*>(sm.a[j])[g] = av;
+        if (g == 0) sm.b[j] = bv;
+    }
+    lds_barrier();
+    // one wave per token: the L2 norms of q and k and k^.q^
+    for (int t = wv; t < n; t += G::NT / 64) {
+        float sqq = 0.0f, skk = 0.0f, sqk = 0.0f;
+#pragma unroll
+        for (int i = lane; i < D; i += 64) {
+            const float qv = sm.z[t][i], kv = sm.z[t][D + i];
+            sqq = fmaf(qv, qv, sqq);
+            skk = fmaf(kv, kv, skk);
+            sqk = fmaf(qv, kv, sqk);
+        }
+        sqq = wave_sum(sqq);
+        skk = wave_sum(skk);
+        sqk = wave_sum(sqk);
+        if (lane == 0) {
+            const float rq = p.scale * rsqrtf(sqq + 1e-6f), rk = rsqrtf(skk + 1e-6f);
+            sm.rq[t] = rq;
+            sm.rk[t] = rk;
+            sm.kq[t] = sqk * rq * rk;
+        }
+    }
+    lds_barrier();
+}
+
+// The state-dependent part of token c0 + t: fade, both reductions, delta
+// correction, readout, rank-1 write.  Two barriers.
+template <typename TS, class MG, int D>
+__device__ __forceinline__ void multi_token(float (&sreg)[MG::G::RPL][MG::G::IO_VEC], const Ptrs& p, int T,
+                                            int m, int h, int tok, int t, MultiSmem<MG, D>& sm) {
+    typedef typename MG::G G;
     constexpr int NT = G::NT, COLS = G::COLS, CG = G::CG, RPL = G::RPL, VEC = G::IO_VEC;
     constexpr int NWAVES = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int cg = lane % CG, rw = lane / CG;
-    float* const s_q = sm.z;
-    float* const s_k = sm.z + D;
-    float* const s_v = sm.z + 2 * D;
-
-    if (tid < G::NG) {
-        reinterpret_cast<f32x4*>(sm.z)[tid] =
-            f32x4{conv_silu(u32x2{w01.x, w01.y}, bf16_lo(t0.x), bf16_lo(t1.x), bf16_lo(t2.x), bf16_lo(in.x.x)),
-                  conv_silu(u32x2{w01.z, w01.w}, bf16_hi(t0.x), bf16_hi(t1.x), bf16_hi(t2.x), bf16_hi(in.x.x)),
-                  conv_silu(u32x2{w23.x, w23.y}, bf16_lo(t0.y), bf16_lo(t1.y), bf16_lo(t2.y), bf16_lo(in.x.y)),
-                  conv_silu(u32x2{w23.z, w23.w}, bf16_hi(t0.y), bf16_hi(t1.y), bf16_hi(t2.y), bf16_hi(in.x.y))};
-        t0 = t1;
-        t1 = t2;
-        t2 = in.x;
-    }
-    const int ag = tid - (NT - D / 4);
-    if (ag >= 0) reinterpret_cast<f32x4*>(sm.a)[ag] = in.a;
-    lds_barrier();
-    if constexpr (FIRST) {
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) G::IO::unpack(raw[r], sreg[r]);
-    }
-
-    float sqq = 0.0f, skk = 0.0f, sqk = 0.0f;
-#pragma unroll
-    for (int i = lane; i < D; i += 64) {
-        const float qv = s_q[i], kv = s_k[i];
-        sqq = fmaf(qv, qv, sqq);
-        skk = fmaf(kv, kv, skk);
-        sqk = fmaf(qv, kv, sqk);
-    }
-    sqq = wave_sum(sqq);
-    skk = wave_sum(skk);
-    sqk = wave_sum(sqk);
-    const float rq = p.scale * rsqrtf(sqq + 1e-6f);
-    const float rk = rsqrtf(skk + 1e-6f);
-    const float kq = sqk * rq * rk;
+    const float rq = sm.rq[t], rk = sm.rk[t], kq = sm.kq[t], b = sm.b[t];
 
     float kk[RPL], u[VEC], wq[VEC];
 #pragma unroll
@@ -626,8 +658,8 @@ __device__ __forceinline__ void token_step(const TokIn& in, u32x2& t0, u32x2& t1
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const int i = G::row(wv, rw, r);
-        const float a = sm.a[i], qq = s_q[i] * rq;
-        kk[r] = s_k[i] * rk;
+        const float a = sm.a[t][i], qq = sm.z[t][i] * rq;
+        kk[r] = sm.z[t][D + i] * rk;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const float sv = sreg[r][e] * a;
@@ -646,7 +678,8 @@ __device__ __forceinline__ void token_step(const TokIn& in, u32x2& t0, u32x2& t1
     }
 
     float d[VEC];
-    uint16_t* const ou = p.o + ((size_t)m * T + t) * ((size_t)p.H * D) + (size_t)h * D;
+    uint16_t* const ou = p.o + ((size_t)m * T + tok) * ((size_t)p.H * D) + (size_t)h * D;
+    const float* const sv_ = sm.z[t] + 2 * D;
     if constexpr (NWAVES > 1) {
         static_assert(2 * COLS <= NT, "u and w sums need 2*COLS threads");
         if (rw == 0) {
@@ -661,7 +694,7 @@ __device__ __forceinline__ void token_step(const TokIn& in, u32x2& t0, u32x2& t1
             float U = 0.0f;
 #pragma unroll
             for (int w = 0; w < NWAVES; ++w) U += sm.red[w][0][tid];
-            sm.d[tid] = in.b * (s_v[tid] - U);
+            sm.d[tid] = b * (sv_[tid] - U);
         } else if (tid < 2 * COLS) {
             float W = 0.0f;
 #pragma unroll
@@ -674,14 +707,12 @@ __device__ __forceinline__ void token_step(const TokIn& in, u32x2& t0, u32x2& t1
         if (tid < COLS) ou[tid] = (uint16_t)f32_to_bf16_rne(fmaf(sm.d[tid], kq, sm.w[tid]));
     } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) d[e] = in.b * (s_v[cg * VEC + e] - u[e]);
+        for (int e = 0; e < VEC; ++e) d[e] = b * (sv_[cg * VEC + e] - u[e]);
         if (rw == 0) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 ou[cg * VEC + e] = (uint16_t)f32_to_bf16_rne(fmaf(d[e], kq, wq[e]));
         }
-        // the next token overwrites the vectors this one read
-        lds_barrier();
     }
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
@@ -691,33 +722,20 @@ __device__ __forceinline__ void token_step(const TokIn& in, u32x2& t0, u32x2& t1
 
 // One workgroup per (stream, head), T >= 1 tokens; x [M][T][3][H*D],
 // alpha [M][T][H][D], beta [M][T][H], o [M][T][H][D].
-template <typename TS, int D, int NWAVES, int VEC, int RMAP>
+template <typename TS, int D, int NWAVES, int VEC, int RMAP, int TCMAX = 16>
 __global__ __launch_bounds__(NWAVES * 64)
 void decode_multi_kernel(const Ptrs p, const int units, const int T)
 {
-    typedef Geo<TS, D, 1, NWAVES, VEC, RMAP> G;
-    __shared__ Smem<G, D> sm;
+    typedef MultiGeo<TS, D, NWAVES, VEC, RMAP, TCMAX> MG;
+    typedef typename MG::G G;
+    __shared__ MultiSmem<MG, D> sm;
     const int unit = (int)blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int cg = lane % G::CG, rw = lane / G::CG;
     const int m = unit / p.H, h = unit - m * p.H;
     const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
-    const size_t ch = tid < G::NG ? group_channel<G, D>(tid, h, 0, HD) : 0;
 
-    u32x2 t0, t1, t2;
-    u32x4 w01, w23;
-    if (tid < G::NG) {
-        const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
-        t0 = ld8(ci);
-        t1 = ld8(ci + C3);
-        t2 = ld8(ci + 2 * C3);
-        const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
-        w01 = wp[0];
-        w23 = wp[1];
-    }
-    TokIn cur, nxt;
-    load_token<G, D>(cur, p, T, m, h, ch, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    // the state loads go out first; the first chunk's small loads overlap them
     TS* const st = static_cast<TS*>(p.state) + (size_t)unit * D * D + cg * G::IO_VEC;
     typename G::raw_t raw[G::RPL];
 #pragma unroll
@@ -725,25 +743,36 @@ void decode_multi_kernel(const Ptrs p, const int units, const int T)
     __builtin_amdgcn_sched_barrier(0);
     float sreg[G::RPL][G::IO_VEC];
 
-    // token 0, then the rest; the next token's loads go out first (the last
-    // token re-reads its own inputs: a placeholder in bounds)
-    load_token<G, D>(nxt, p, T, m, h, ch, T > 1 ? 1 : 0);
-    __builtin_amdgcn_sched_barrier(0);
-    token_step<TS, G, D, true>(cur, t0, t1, t2, w01, w23, raw, sreg, p, T, m, h, 0, sm);
-    for (int t = 1; t < T; ++t) {
-        cur = nxt;
-        load_token<G, D>(nxt, p, T, m, h, ch, t + 1 < T ? t + 1 : t);
-        __builtin_amdgcn_sched_barrier(0);
-        token_step<TS, G, D, false>(cur, t0, t1, t2, w01, w23, raw, sreg, p, T, m, h, t, sm);
+    // the first chunk is peeled: the raw state registers die at the unpack
+    {
+        const int n = min(MG::TC, T);
+        multi_chunk<MG, D>(p, T, m, h, 0, n, sm);
+#pragma unroll
+        for (int r = 0; r < G::RPL; ++r) G::IO::unpack(raw[r], sreg[r]);
+        for (int t = 0; t < n; ++t) multi_token<TS, MG, D>(sreg, p, T, m, h, t, t, sm);
+        // the next chunk overwrites the vectors the last token read
+        lds_barrier();
+    }
+    for (int c0 = MG::TC; c0 < T; c0 += MG::TC) {
+        const int n = min(MG::TC, T - c0);
+        multi_chunk<MG, D>(p, T, m, h, c0, n, sm);
+        for (int t = 0; t < n; ++t) multi_token<TS, MG, D>(sreg, p, T, m, h, c0 + t, t, sm);
+        lds_barrier();
     }
 
 #pragma unroll
     for (int r = 0; r < G::RPL; ++r) G::IO::store(st + (size_t)G::row(wv, rw, r) * D, sreg[r]);
-    if (tid < G::NG) {
+    // conv state after T tokens: sequence positions T-3, T-2, T-1 (a
+    // position < 0 is one of the cached taps, read before it is overwritten)
+    if (tid < MG::NGT) {
+        const size_t ch = group_channel<G, D>(tid, h, 0, HD);
+        const u32x2 n0 = seq_input(p, T, m, C3, ch, T - 3);
+        const u32x2 n1 = seq_input(p, T, m, C3, ch, T - 2);
+        const u32x2 n2 = seq_input(p, T, m, C3, ch, T - 1);
         uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + ch;
-        st8(co, t0);
-        st8(co + C3, t1);
-        st8(co + 2 * C3, t2);
+        st8(co, n0);
+        st8(co + C3, n1);
+        st8(co + 2 * C3, n2);
     }
 }
 
@@ -889,7 +918,7 @@ static hipError_t launch_multi(const StepArgs& a) {
                            dim3((unsigned)units), dim3(NWAVES * 64), args, 0, (hipStream_t)a.stream);
 }
 
-// T tokens per launch: the whole-head shapes of the single-token step.
+// T tokens per launch, one workgroup per head.
 hipError_t launch_decode_multi(const StepArgs& a) {
     const bool f32 = a.state_dtype == 0;
     switch (a.D) {
@@ -897,10 +926,10 @@ hipError_t launch_decode_multi(const StepArgs& a) {
     case 32: return f32 ? launch_multi<float, 32, 1, 4, 0>(a) : launch_multi<uint16_t, 32, 1, 8, 0>(a);
     case 64: return f32 ? launch_multi<float, 64, 2, 4, 0>(a) : launch_multi<uint16_t, 64, 2, 8, 0>(a);
     case 128:
-        if (f32)
-            return (long)a.M * a.H >= 2048 ? launch_multi<float, 128, 16, 4, 0>(a)
-                                           : launch_multi<float, 128, 8, 4, 0>(a);
-        return launch_multi<uint16_t, 128, 8, 8, 1>(a);
+        // 4 waves per head (16 or 8 rows per lane), each wave a band of rows:
+        // the token loop is latency-bound, so more heads per CU beat more
+        // waves per head (measured)
+        return f32 ? launch_multi<float, 128, 4, 4, 1>(a) : launch_multi<uint16_t, 128, 4, 8, 1>(a);
     default: return hipErrorInvalidValue;
     }
 }
