@@ -99,6 +99,8 @@ class Oracle:
         lib.kda_oracle_layer_step.restype = i
         lib.kda_oracle_decode_multi.argtypes = [i, i, i, i, p, p, p, p, p, p, p, d, d, p]
         lib.kda_oracle_decode_multi.restype = i
+        lib.kda_oracle_sequence_gated.argtypes = [i, i, i, i, p, p, p, p, p, p, p, p, p, i, d, d, d, p]
+        lib.kda_oracle_sequence_gated.restype = i
         self.lib = lib
 
     def max_threads(self) -> int:
@@ -253,6 +255,26 @@ class Oracle:
                                               float(eps), _ptr(o))
         if rc != 0:
             raise RuntimeError(f"kda_oracle_decode_multi failed ({rc})")
+        return S, cs_out, o
+
+
+    def sequence_gated(self, S, x, w, cs, f, A_log, dt_bias, beta_logit, scale,
+                       kind=GATE_BOUNDED, lower_bound=-5.0, eps=L2NORM_EPS):
+        """T tokens per stream with raw gate inputs: x [M,T,3,H*D], f [M,T,H*D],
+        beta_logit [M,T,H]; A_log [H], dt_bias [H*D].  Returns (S_new, cs_new, o [M,T,H,D])."""
+        S = _f64(S).copy()
+        M, H, D, _ = S.shape
+        x, w, cs = _f64(x), _f64(w), _f64(cs)
+        f, A_log, dt_bias, beta_logit = _f64(f), _f64(A_log), _f64(dt_bias), _f64(beta_logit)
+        T = x.shape[1]
+        assert x.shape == (M, T, 3, H * D) and f.shape == (M, T, H * D) and beta_logit.shape == (M, T, H)
+        cs_out = np.empty_like(cs)
+        o = np.empty((M, T, H, D))
+        rc = self.lib.kda_oracle_sequence_gated(T, M, H, D, _ptr(S), _ptr(x), _ptr(w), _ptr(cs), _ptr(cs_out),
+                                                _ptr(f), _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit),
+                                                int(kind), float(lower_bound), float(scale), float(eps), _ptr(o))
+        if rc != 0:
+            raise RuntimeError(f"kda_oracle_sequence_gated failed ({rc})")
         return S, cs_out, o
 
 

@@ -407,3 +407,37 @@ int kda_oracle_decode_multi(int T, int M, int H, int D, double *S, const double 
     free(xt); free(at); free(bt); free(ot);
     return rc;
 }
+
+/*
+ * T consecutive tokens of M streams with raw gate inputs: token t of every
+ * stream goes through kda_oracle_decode_step_gated with the state and conv
+ * state left by token t - 1 ([DD] 8.2.4 steps 2-6 over a sequence; 8.2.5
+ * computes the same recurrence chunk by chunk).
+ *
+ *   x [M][T][3][H*D]   f [M][T][H*D]   blogit [M][T][H]   o [M][T][H][D]
+ *   A_log [H], dt_bias [H*D]; the rest as kda_oracle_decode_step_gated.
+ */
+int kda_oracle_sequence_gated(int T, int M, int H, int D, double *S, const double *x,
+                              const double *w, const double *cs_in, double *cs_out,
+                              const double *f, const double *A_log, const double *dt_bias,
+                              const double *blogit, int kind, double lower_bound, double scale,
+                              double eps, double *o)
+{
+    if (T < 0 || M < 0 || H < 1 || D < 1)
+        return 1;
+    const size_t HD = (size_t)H * D, C = 3 * HD;
+    if (cs_out != cs_in)
+        memcpy(cs_out, cs_in, sizeof(double) * (size_t)M * 3 * C);
+    int rc = 0;
+    for (int m = 0; m < M && rc == 0; ++m) {
+        double *Sm = S + (size_t)m * H * D * D;
+        double *cm = cs_out + (size_t)m * 3 * C;
+        for (int t = 0; t < T && rc == 0; ++t) {
+            const size_t mt = (size_t)m * T + t;
+            rc = kda_oracle_decode_step_gated(1, H, D, Sm, x + mt * C, w, cm, cm, f + mt * HD, A_log,
+                                              dt_bias, blogit + mt * H, kind, lower_bound, scale,
+                                              eps, o + mt * HD);
+        }
+    }
+    return rc;
+}

@@ -586,6 +586,35 @@ def pin_multi_token(orc, M=2, H=2, D=8, T=5, seed=40):
     _close(o1[m, :, h], Oc, 1e-12, "outputs vs chunk form")
 
 
+def pin_sequence_gated(orc, M=2, H=3, D=8, T=6, seed=41):
+    """sequence_gated over T tokens = T single gated steps, and = the
+    ungated multi-token call fed with the gate's alpha and sigmoid(logit)."""
+    rng = np.random.default_rng(seed)
+    S0 = rng.standard_normal((M, H, D, D)) * 0.1
+    x = rng.standard_normal((M, T, 3, H * D))
+    w = rng.standard_normal((3 * H * D, 4)) * 0.5
+    cs0 = rng.standard_normal((M, 3, 3 * H * D))
+    f = rng.standard_normal((M, T, H * D))
+    A = rng.uniform(-0.5, 0.5, H)
+    b = rng.normal(-4.0, 1.0, H * D)
+    bl = rng.standard_normal((M, T, H))
+    S1, cs1, o1 = orc.sequence_gated(S0, x, w, cs0, f, A, b, bl, 0.3, lower_bound=-5.0)
+    S, cs = S0, cs0
+    for t in range(T):
+        S, cs, o = orc.decode_step_gated(S, x[:, t], w, cs, f[:, t], A, b, bl[:, t], 0.3, lower_bound=-5.0)
+        _close(o1[:, t], o, 1e-14, f"gated token {t}")
+    _close(S1, S, 1e-14, "gated sequence state")
+    assert np.array_equal(cs1, cs)
+    alpha = np.empty((M, T, H, D))
+    for m in range(M):
+        for t in range(T):
+            for h in range(H):
+                alpha[m, t, h] = orc.gate(f[m, t, h * D:(h + 1) * D], A[h], b[h * D:(h + 1) * D])
+    S2, _, o2 = orc.decode_multi(S0, x, w, cs0, alpha, orc.beta(bl), 0.3)
+    _close(S2, S1, 1e-14, "gated sequence vs multi with gate alpha")
+    _close(o2, o1, 1e-14, "gated sequence outputs vs multi")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_unrolled_product,
@@ -609,4 +638,5 @@ ALL_PINS = [
     pin_gated_rmsnorm,
     pin_gated_step_wiring,
     pin_multi_token,
+    pin_sequence_gated,
 ]
