@@ -3,7 +3,7 @@
 
     python -m hybrid_linear_attention_kda_amd.build
 
-Compiles ``csrc/kda_kernels.hip`` and ``csrc/kda_api.cpp``, and separately
+Compiles ``csrc/kda_kernels.hip``, ``csrc/kda_prefill.hip`` and ``csrc/kda_api.cpp``, and separately
 ``csrc/kda_probe.hip``, with hipcc for gfx950 only.  Packed-FP32
 instructions are switched off for device code.
 """
@@ -18,8 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libkda.so")
-SOURCES = [os.path.join(CSRC, "kda_kernels.hip"), os.path.join(CSRC, "kda_api.cpp")]
-HEADERS = [os.path.join(INCLUDE, "kda.h"), os.path.join(CSRC, "kda_launch.h")]
+SOURCES = [os.path.join(CSRC, "kda_kernels.hip"), os.path.join(CSRC, "kda_prefill.hip"),
+           os.path.join(CSRC, "kda_api.cpp")]
+HEADERS = [os.path.join(INCLUDE, "kda.h"), os.path.join(CSRC, "kda_launch.h"), os.path.join(CSRC, "kda_device.h")]
 PROBE_LIBRARY = os.path.join(PKG, "libkda_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "kda_probe.hip")]
 

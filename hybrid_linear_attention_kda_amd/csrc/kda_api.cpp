@@ -289,6 +289,49 @@ int kda_decode_multi(int T, int M, int H, int D, int state_dtype, void* state, c
     return map_hip(kda::launch_decode_multi(a));
 }
 
+int kda_prefill_gated(int L, int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                      const void* conv_w, const void* conv_in, void* conv_out, const void* f_gate,
+                      const float* A_log, const float* dt_bias, const void* beta_logit,
+                      float gate_lower_bound, float scale, void* o, void* stream) {
+    if (L < 0) return KDA_ERR_ARG;
+    int rc = check_common(M, H, D, state_dtype, scale);
+    if (rc != KDA_OK) return rc;
+    if (D != 128) return KDA_ERR_SHAPE;
+    if (!(isfinite(gate_lower_bound) && gate_lower_bound >= -5.0f && gate_lower_bound < 0.0f))
+        return KDA_ERR_ARG;
+    if (M == 0 || L == 0) return KDA_OK;
+    const void* need[] = {state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt_bias, beta_logit, o};
+    for (const void* p : need)
+        if (!p) return KDA_ERR_NULL;
+    for (const void* p : need)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    StepSizes sz;
+    rc = step_sizes(M, H, D, state_dtype, &sz);
+    if (rc != KDA_OK) return rc;
+    size_t bx, bf, bb, bo;
+    const long HD = (long)H * D;
+    if (!checked_bytes((long)M * L, 3, HD, 1, 2, &bx) || !checked_bytes((long)M * L, HD, 1, 1, 2, &bf) ||
+        !checked_bytes((long)M * L, H, 1, 1, 2, &bb) || !checked_bytes((long)M * L, HD, 1, 1, 2, &bo))
+        return KDA_ERR_ARG;
+    const Range rs = span(state, sz.state), ro = span(o, bo), rco = span(conv_out, sz.conv);
+    const Range inputs[] = {span(x_qkv, bx), span(conv_w, sz.w), span(conv_in, sz.conv), span(f_gate, bf),
+                            span(A_log, sz.A_log), span(dt_bias, sz.dt_bias), span(beta_logit, bb)};
+    for (const Range& r : inputs)
+        if (overlap(rs, r) || overlap(ro, r)) return KDA_ERR_ALIAS;
+    if (overlap(rs, ro) || overlap(rs, rco) || overlap(ro, rco)) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 7; ++i) {
+        if (i == 2 && conv_out == conv_in) continue;
+        if (overlap(rco, inputs[i])) return KDA_ERR_ALIAS;
+    }
+    kda::StepArgs a{};
+    a.M = M; a.H = H; a.D = D; a.T = L; a.state_dtype = state_dtype; a.nsplit = 1;
+    a.state = state; a.x = x_qkv; a.conv_w = conv_w; a.conv_in = conv_in; a.conv_out = conv_out;
+    a.fgate = f_gate; a.A_log = A_log; a.dt_bias = dt_bias; a.beta_logit = beta_logit;
+    a.gate_kind = KDA_GATE_BOUNDED; a.lower_bound = gate_lower_bound; a.scale = scale; a.o = o;
+    a.stream = stream;
+    return map_hip(kda::launch_prefill(a));
+}
+
 int kda_conv_step(int M, int C, const void* x, const void* conv_w, const void* conv_in,
                   void* conv_out, float* y, void* stream) {
     if (M < 0 || C < 1 || (C % 8) != 0) return KDA_ERR_ARG;
@@ -351,6 +394,6 @@ const char* kda_status_string(int status) {
     }
 }
 
-int kda_version(void) { return 10100; }
+int kda_version(void) { return 10200; }
 
 }  // extern "C"

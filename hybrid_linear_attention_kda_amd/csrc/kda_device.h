@@ -1,0 +1,157 @@
+// kda_device.h -- device helpers shared by the gfx950 kernels of the KDA
+// library (decode step and chunked prefill).  Internal, not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_launch.h"
+
+namespace kda {
+
+// Kernel arguments of every decode / prefill launch (pointers already
+// validated by the host).
+struct Ptrs {
+    int H;
+    void* state;
+    const uint16_t* x;
+    const uint16_t* conv_w;
+    const uint16_t* conv_in;
+    uint16_t* conv_out;
+    const float* qkv;
+    const float* alpha;
+    const float* beta;
+    float scale;
+    uint16_t* o;
+    // gated prologue (MODE >= 1): raw gate inputs instead of alpha / beta
+    const uint16_t* fgate;     // bf16 [M][H*D] forget-gate projection
+    const float* A_log;        // [H]
+    const float* dt_bias;      // [H*D]
+    const uint16_t* blogit;    // bf16 [M][H] write-strength logits
+    int gate_kind;             // 0: bounded sigmoid, 1: softplus
+    float lower_bound;         // gate_kind 0 only
+    // gated RMSNorm epilogue (MODE == 2): o is replaced by y
+    const uint16_t* ogate;     // bf16 [M][H*D] output-gate projection
+    const float* norm_w;       // [D]
+    float norm_eps;
+};
+
+inline Ptrs make_ptrs(const StepArgs& a) {
+    Ptrs p;
+    p.H = a.H;
+    p.state = a.state;
+    p.x = static_cast<const uint16_t*>(a.x);
+    p.conv_w = static_cast<const uint16_t*>(a.conv_w);
+    p.conv_in = static_cast<const uint16_t*>(a.conv_in);
+    p.conv_out = static_cast<uint16_t*>(a.conv_out);
+    p.qkv = a.qkv;
+    p.alpha = a.alpha;
+    p.beta = a.beta;
+    p.scale = a.scale;
+    p.o = static_cast<uint16_t*>(a.o);
+    p.fgate = static_cast<const uint16_t*>(a.fgate);
+    p.A_log = a.A_log;
+    p.dt_bias = a.dt_bias;
+    p.blogit = static_cast<const uint16_t*>(a.beta_logit);
+    p.gate_kind = a.gate_kind;
+    p.lower_bound = a.lower_bound;
+    p.ogate = static_cast<const uint16_t*>(a.out_gate);
+    p.norm_w = a.norm_w;
+    p.norm_eps = a.norm_eps;
+    return p;
+}
+
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- helpers --
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+
+// f32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Workgroup barrier that orders LDS only: global loads issued before it stay
+// in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// One lane's share of a state row: VEC consecutive elements, 16 (or 8) bytes.
+template <typename TS, int VEC> struct Chunk;
+
+template <> struct Chunk<float, 4> {
+    typedef f32x4 raw_t;
+    static __device__ __forceinline__ raw_t load(const float* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    }
+    static __device__ __forceinline__ void unpack(const raw_t& r, float* f) {
+        f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float* f) {
+        f32x4 r = {f[0], f[1], f[2], f[3]};
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+    }
+};
+
+template <> struct Chunk<uint16_t, 8> {
+    typedef u32x4 raw_t;
+    static __device__ __forceinline__ raw_t load(const uint16_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    }
+    static __device__ __forceinline__ void unpack(const raw_t& r, float* f) {
+        f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x); f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+        f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z); f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float* f) {
+        u32x4 r = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                   pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+        __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+    }
+};
+
+template <> struct Chunk<uint16_t, 4> {
+    typedef u32x2 raw_t;
+    static __device__ __forceinline__ raw_t load(const uint16_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    }
+    static __device__ __forceinline__ void unpack(const raw_t& r, float* f) {
+        f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x); f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float* f) {
+        u32x2 r = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+        __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(p));
+    }
+};
+
+// Short causal conv (kernel 4) + SiLU for one channel, "GLM-5.3 deep dive"
+// 8.2.4 step 2.  w4 packs the channel's 4 bf16 taps (tap 3 = current token).
+__device__ __forceinline__ float conv_silu(u32x2 w4, float t0, float t1, float t2, float xc) {
+    float y = bf16_lo(w4.x) * t0;
+    y = fmaf(bf16_hi(w4.x), t1, y);
+    y = fmaf(bf16_lo(w4.y), t2, y);
+    y = fmaf(bf16_hi(w4.y), xc, y);
+    return y / (1.0f + expf(-y));
+}
+
+}  // namespace kda

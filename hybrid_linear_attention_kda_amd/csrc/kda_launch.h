@@ -41,6 +41,7 @@ hipError_t launch_recurrent_step(const StepArgs& a);
 hipError_t launch_decode_step_gated(const StepArgs& a);
 hipError_t launch_layer_step(const StepArgs& a);
 hipError_t launch_decode_multi(const StepArgs& a);
+hipError_t launch_prefill(const StepArgs& a);
 hipError_t launch_conv_step(int M, int C, const void* x, const void* w, const void* cin,
                             void* cout, float* y, void* stream);
 

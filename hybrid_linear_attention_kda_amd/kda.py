@@ -24,8 +24,8 @@ KDA_GATE_BOUNDED, KDA_GATE_SOFTPLUS = 0, 1
 
 #: every symbol ``include/kda.h`` declares
 EXPORTS = ("kda_decode_step", "kda_decode_step_split", "kda_decode_step_gated",
-           "kda_decode_layer_step", "kda_decode_multi", "kda_conv_step", "kda_recurrent_step",
-           "kda_status_string", "kda_version")
+           "kda_decode_layer_step", "kda_decode_multi", "kda_prefill_gated", "kda_conv_step",
+           "kda_recurrent_step", "kda_status_string", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -58,6 +58,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_layer_step.restype = i
     lib.kda_decode_multi.argtypes = [i] + step
     lib.kda_decode_multi.restype = i
+    lib.kda_prefill_gated.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, fp, fp, vp, f, f, vp, vp]
+    lib.kda_prefill_gated.restype = i
     lib.kda_conv_step.argtypes = [i, i, vp, vp, vp, vp, fp, vp]
     lib.kda_conv_step.restype = i
     lib.kda_recurrent_step.argtypes = [i, i, i, i, vp, fp, fp, fp, f, vp, vp]
@@ -268,3 +270,33 @@ def kda_decode_multi(state, x_qkv, conv_w, conv_in, conv_out, alpha, beta, scale
            lib.kda_decode_multi(T, M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w),
                                 _p(conv_in), _p(conv_out), _p(alpha), _p(beta), float(scale), _p(o),
                                 _stream(dev, stream)))
+
+
+def kda_prefill_gated(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt_bias, beta_logit,
+                      scale, o, lower_bound=-5.0, stream=None):
+    """L tokens per stream, chunkwise on matrix cores (see ``kda_prefill_gated``
+    in kda.h): x_qkv [M,L,3,H*D] bf16, f_gate [M,L,H*D] bf16, A_log [H] f32,
+    dt_bias [H*D] f32, beta_logit [M,L,H] bf16, o [M,L,H,D] bf16; D = 128."""
+    lib = load()
+    if state.dim() != 4 or x_qkv.dim() != 4:
+        raise ValueError("state must be [M, H, D, D] and x_qkv [M, L, 3, H*D]")
+    M, H, D, _ = state.shape
+    L = x_qkv.shape[1]
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("state must be a GPU tensor")
+    _need(state, "state", (M, H, D, D), state.dtype, dev)
+    _need(x_qkv, "x_qkv", (M, L, 3, H * D), torch.bfloat16, dev)
+    _need(conv_w, "conv_w", (3 * H * D, 4), torch.bfloat16, dev)
+    _need(conv_in, "conv_in", (M, 3, 3 * H * D), torch.bfloat16, dev)
+    _need(conv_out, "conv_out", (M, 3, 3 * H * D), torch.bfloat16, dev)
+    _need(f_gate, "f_gate", (M, L, H * D), torch.bfloat16, dev)
+    _need(A_log, "A_log", (H,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * D,), torch.float32, dev)
+    _need(beta_logit, "beta_logit", (M, L, H), torch.bfloat16, dev)
+    _need(o, "o", (M, L, H, D), torch.bfloat16, dev)
+    _check("kda_prefill_gated",
+           lib.kda_prefill_gated(L, M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w),
+                                 _p(conv_in), _p(conv_out), _p(f_gate), _p(A_log), _p(dt_bias),
+                                 _p(beta_logit), float(lower_bound), float(scale), _p(o),
+                                 _stream(dev, stream)))

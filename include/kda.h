@@ -198,6 +198,43 @@ int kda_decode_multi(int T, int M, int H, int D, int state_dtype,
                      void *o, void *stream);
 
 /*
+ * kda_prefill_gated -- L consecutive tokens of each of M streams (a prompt
+ * or a long continuation), computed chunk by chunk in the WY / UT form of
+ * "GLM-5.3 deep dive" 8.2.5 on matrix cores: the same recurrence as L calls
+ * of kda_decode_step_gated (conv + SiLU, L2 norms, bounded forget gate,
+ * beta = sigmoid(logit), gated delta rule, readout), reordered into matrix
+ * products over chunks of 16 tokens.
+ *
+ *  L          tokens per stream, >= 0 (L == 0 or M == 0: nothing is touched).
+ *  D          must be 128.
+ *  x_qkv      [M][L][3][H*D]  bf16 pre-conv q|k|v.
+ *  f_gate     [M][L][H*D]     bf16 raw forget-gate projection.
+ *  A_log [H], dt_bias [H*D]   f32, as kda_decode_step_gated.
+ *  beta_logit [M][L][H]       bf16.
+ *  gate_lower_bound           in [-5, 0): the bounded gate only.  Within a
+ *             16-token chunk the cumulative log-decay is then >= -80, so the
+ *             chunk's decay products and their inverses stay inside f32's
+ *             range (8.2.3 implementation notes on the -5 bound).
+ *  o          [M][L][H][D]    bf16 output of every token.
+ *  state, conv_w, conv_in, conv_out, scale as kda_decode_step (conv_out may
+ *  be conv_in; it receives the last three raw inputs).
+ *
+ * One workgroup per (stream, head) sweeps its chunks in order, so M*H
+ * should be at least the device's compute-unit count for a full device.
+ * Results agree with the token-by-token recurrence to the rounding of the
+ * reordered f32 arithmetic (see the tests), not bit for bit.  Returns a
+ * KDA_* status (KDA_ERR_SHAPE for D != 128, KDA_ERR_ARG for a lower bound
+ * outside [-5, 0)).
+ */
+int kda_prefill_gated(int L, int M, int H, int D, int state_dtype,
+                      void *state, const void *x_qkv, const void *conv_w,
+                      const void *conv_in, void *conv_out,
+                      const void *f_gate, const float *A_log,
+                      const float *dt_bias, const void *beta_logit,
+                      float gate_lower_bound, float scale, void *o,
+                      void *stream);
+
+/*
  * kda_conv_step -- the conv stage alone, over C independent channels
  * ("GLM-5.3 deep dive", 8.2.4 step 2; one launch over all q|k|v channels).
  *

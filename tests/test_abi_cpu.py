@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert kda.kda_version() == 10100
+    assert kda.kda_version() == 10200
     for code in range(8):
         s = kda.kda_status_string(code)
         assert s and s != "unknown status"
@@ -240,6 +240,32 @@ def test_multi_errors(lib):
     # o is inside it at T = 64
     q = list(p); q[5] = q[7] + 64 * 1024
     assert call(T=64, ptrs=q) == binding.KDA_ERR_ALIAS
+
+
+# ------------------------------------------------------------------ prefill --
+def test_prefill_errors(lib):
+    # state, x, w, cin, cout, f, A_log, dt_bias, beta_logit, o
+    p = [fake(i) for i in range(10)]
+
+    def call(L=32, M=1, H=64, D=128, sdt=0, ptrs=p, lb=-5.0, scale=0.125):
+        s, x, w, ci, co, f, A, b, bl, o = ptrs
+        return lib.kda_prefill_gated(L, M, H, D, sdt, s, x, w, ci, co, f, A, b, bl, lb, scale, o, None)
+    assert call(L=-1) == binding.KDA_ERR_ARG
+    assert call(D=64) == binding.KDA_ERR_SHAPE
+    assert call(sdt=4) == binding.KDA_ERR_DTYPE
+    for lb in (-5.5, 0.0, 0.5, math.nan, -math.inf):
+        assert call(lb=lb) == binding.KDA_ERR_ARG, lb
+    assert call(L=0, ptrs=[None] * 10) == binding.KDA_OK
+    assert call(M=0, ptrs=[None] * 10) == binding.KDA_OK
+    for i in range(10):
+        q = list(p); q[i] = None
+        assert call(ptrs=q) == binding.KDA_ERR_NULL
+        q = list(p); q[i] += 4
+        assert call(ptrs=q) == binding.KDA_ERR_ALIGN
+    q = list(p); q[9] = q[5]            # o over f_gate
+    assert call(ptrs=q) == binding.KDA_ERR_ALIAS
+    q = list(p); q[0] = q[1] + 8192     # state inside x
+    assert call(ptrs=q) == binding.KDA_ERR_ALIAS
 
 
 def test_binding_rejects_host_tensors():

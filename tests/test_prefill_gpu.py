@@ -1,0 +1,117 @@
+"""GPU parity of kda_prefill_gated (chunkwise WY / UT form on matrix cores,
+"GLM-5.3 deep dive" 8.2.5) against the CPU oracle's token-by-token gated
+recurrence over the same sequence.
+
+The chunk form reorders the arithmetic: decay ratios come from cumulative
+sums of up to 16 log-decays and pass through exp, and the state is updated
+by matrix products instead of rank-1 writes.  Tolerances (relative to the
+largest reference magnitude) are those of the per-token step: f32 state
+1e-5 (measured: <= 8.3e-7 over 100 tokens at lower bounds -5 and -1.5),
+bf16 state 4e-3 (one rounding at the end), outputs 4e-3 (one bf16
+rounding: up to 2^-8 of the largest output).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_synth
+import oracle
+from hybrid_linear_attention_kda_amd import kda_prefill_gated
+from kda_gpu_util import TOL_O, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL_STATE_PREFILL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.init()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def sequence(wl, L, layer=0):
+    """Per-token inputs of L tokens stacked on a token axis."""
+    st = [kda_synth.step_inputs(wl, layer, t, DEV) for t in range(L)]
+    gi = [kda_synth.gate_inputs(wl, layer, t, DEV) for t in range(L)]
+    return (torch.stack([s["x"] for s in st], 1).contiguous(),
+            torch.stack([g["f"] for g in gi], 1).contiguous(),
+            torch.stack([g["beta_logit"] for g in gi], 1).contiguous())
+
+
+def run(orc, M, H, L, state_dtype, lb, inplace, name):
+    wl = kda_synth.custom(name, M, H, 128, steps=max(L, 1))
+    li = kda_synth.layer_inputs(wl, 0, DEV, state_dtype)
+    gp = kda_synth.gate_params(wl, 0, DEV)
+    S, w, cs = li["state"], li["conv_w"], li["conv_state"]
+    cout = cs if inplace else torch.empty_like(cs)
+    x, f, bl = sequence(wl, L)
+    o = torch.empty((M, L, H, 128), dtype=torch.bfloat16, device=DEV)
+    S0, cs0 = host(S), host(cs)
+    kda_prefill_gated(S, x, w, cs, cout, f, gp["A_log"], gp["dt_bias"], bl, wl.scale, o, lower_bound=lb)
+    torch.cuda.synchronize()
+    S_ref, cs_ref, o_ref = orc.sequence_gated(S0, host(x), host(w), cs0, host(f), host(gp["A_log"]),
+                                              host(gp["dt_bias"]), host(bl), wl.scale, lower_bound=lb)
+    return S, cout, o, S_ref, cs_ref, o_ref
+
+
+@pytest.mark.parametrize("inplace", [True, False], ids=["conv_inplace", "conv_pingpong"])
+@pytest.mark.parametrize("lb", [-5.0, -1.5])
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,H,L", [(1, 1, 16), (1, 2, 37), (2, 3, 64), (1, 4, 100), (1, 1, 1), (2, 2, 3)])
+def test_prefill_against_oracle(orc, M, H, L, state_dtype, lb, inplace):
+    S, cout, o, S_ref, cs_ref, o_ref = run(orc, M, H, L, state_dtype, lb, inplace, f"prefill_{M}_{H}_{L}")
+    assert np.array_equal(host(cout), cs_ref), "conv state after the sequence"
+    e_s = rel_err(host(S), S_ref)
+    e_o = max(rel_err(host(o[:, t]), o_ref[:, t]) for t in range(L))
+    say(f"prefill ({M},{H},L={L}) {state_dtype} lb={lb}: state {e_s:.3e} o {e_o:.3e}")
+    assert e_s <= (TOL_STATE_PREFILL if state_dtype == "f32" else 4e-3), f"state error {e_s:.3e}"
+    assert e_o <= TOL_O, f"output error {e_o:.3e}"
+
+
+def test_prefill_many_heads_sampled(orc):
+    """M = 4 streams x 64 heads x 256 tokens (the benchmark's launch shape at
+    smaller M): sampled (stream, head) units against the oracle."""
+    M, H, L = 4, 64, 256
+    wl = kda_synth.custom("prefill_wide", M, H, 128, steps=L)
+    li = kda_synth.layer_inputs(wl, 0, DEV, "f32")
+    gp = kda_synth.gate_params(wl, 0, DEV)
+    S, w, cs = li["state"], li["conv_w"], li["conv_state"]
+    x, f, bl = sequence(wl, L)
+    o = torch.empty((M, L, H, 128), dtype=torch.bfloat16, device=DEV)
+    S0, cs0, cw = host(S), host(cs), host(w).reshape(3, H, 128, 4)
+    kda_prefill_gated(S, x, w, cs, cs, f, gp["A_log"], gp["dt_bias"], bl, wl.scale, o)
+    torch.cuda.synchronize()
+    D = 128
+    for (m, h) in [(0, 0), (1, 33), (3, 63), (2, 7)]:
+        sl = slice(h * D, (h + 1) * D)
+        S_ref, _, o_ref = orc.sequence_gated(
+            S0[m, h][None, None], host(x[m]).reshape(L, 3, H, D)[:, :, h].reshape(1, L, 3, D),
+            cw[:, h].reshape(3 * D, 4), cs0[m].reshape(3, 3, H, D)[:, :, h].reshape(1, 3, 3 * D),
+            host(f[m, :, sl])[None], host(gp["A_log"][h:h + 1]), host(gp["dt_bias"][sl]),
+            host(bl[m, :, h:h + 1])[None], wl.scale)
+        assert rel_err(host(S[m, h]), S_ref[0, 0]) <= TOL_STATE_PREFILL, f"state ({m},{h})"
+        assert rel_err(host(o[m, :, h]), o_ref[0, :, 0]) <= TOL_O, f"outputs ({m},{h})"
+    say("prefill M=4 x 64 heads x 256 tokens, sampled units ok")
+
+
+def test_prefill_empty():
+    wl = kda_synth.custom("prefill_empty", 1, 2, 128)
+    li = kda_synth.layer_inputs(wl, 0, DEV, "f32")
+    gp = kda_synth.gate_params(wl, 0, DEV)
+    S = li["state"].clone()
+    e = lambda *s, dt=torch.bfloat16: torch.empty(s, dtype=dt, device=DEV)  # noqa: E731
+    kda_prefill_gated(S, e(1, 0, 3, 256), li["conv_w"], li["conv_state"], li["conv_state"], e(1, 0, 256),
+                      gp["A_log"], gp["dt_bias"], e(1, 0, 2), wl.scale, e(1, 0, 2, 128))
+    torch.cuda.synchronize()
+    assert torch.equal(S, li["state"])
