@@ -9,7 +9,9 @@ HBM, not from the 256 MiB Infinity Cache).  Inputs are synthetic
 q/k/v, alpha, beta per step) rotate across steps.
 
 Headline: M = 32 streams, FP32 state.  Also measured (``secondary``): M = 8
-with FP32 and BF16 state, M = 128 with BF16 state, and M = 1.
+with FP32 and BF16 state, M = 128 with BF16 state, M = 1, the gated and
+layer steps, T = 8 tokens per call, and the chunked prefill (tokens/s and
+FP32 matrix-core TFLOP/s for M streams x L tokens of one layer).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -50,6 +52,19 @@ SIDE_BYTES = {"plain": (393_472, 196_608), "gated": (376_960, 196_608 + 32_768 +
 MULTI_TOKEN_BYTES, MULTI_CALL_BYTES = 98_560, 294_912
 MULTI_T = 8
 CONV_W_BYTES = 196_608
+# chunked prefill (16-token chunks, D = 128), per (chunk, head): the
+# intra-chunk products A and P 2 x 2 C^2 D, the UT products W = M (Gamma K)
+# and U = M V 2 x 2 C^2 D, the state products W S and (Gamma Q) S
+# 2 x 2 C D^2, P Delta 2 C^2 D, the state update 2 C D^2 -> 1,900,544 flops
+PREFILL_FLOPS_PER_CHUNK_HEAD = 1_900_544
+PREFILL_CHUNK = 16
+# per stream and token: x 49,152 + f 16,384 + beta logit 128 + o 16,384 read or
+# written; per stream the conv state 294,912; per layer conv w, dt_bias, A_log
+PREFILL_TOKEN_BYTES, PREFILL_STREAM_BYTES = 82_048, 294_912
+PREFILL_LAYER_BYTES = 196_608 + 32_768 + 256
+MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X dense FP32 matrix
+# (streams, tokens per stream, state dtype) of the prefill lines
+PREFILL_SHAPES = ((8, 2048, "f32"), (1, 8192, "f32"), (32, 1024, "bf16"))
 
 
 def log(msg):
@@ -197,6 +212,61 @@ def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain", T=1):
     import torch
     torch.cuda.empty_cache()
     return out
+
+
+def measure_prefill(M, L, state_dtype, steps, warmup, H=64, D=128):
+    """kda_prefill_gated over M streams x L tokens of one layer, launched
+    `steps` times on the same buffers (state and conv state carried along)."""
+    import torch
+
+    import kda_synth
+    from hybrid_linear_attention_kda_amd import kda
+    lib = kda.load()
+    wl = kda_synth.custom(f"prefill_m{M}_l{L}", M, H, D, steps=L, seed=7)
+    li = kda_synth.layer_inputs(wl, 0, "cuda:0", state_dtype)
+    gp = kda_synth.gate_params(wl, 0, "cuda:0")
+    seq = kda_synth.sequence_inputs(wl, 0, L, "cuda:0")
+    o = torch.empty((M, L, H, D), dtype=torch.bfloat16, device="cuda:0")
+    torch.cuda.synchronize()
+    vp = ctypes.c_void_p
+    sdt = kda.KDA_STATE_F32 if state_dtype == "f32" else kda.KDA_STATE_BF16
+    stream = torch.cuda.Stream()
+    args = (L, M, H, D, sdt, vp(li["state"].data_ptr()), vp(seq["x"].data_ptr()),
+            vp(li["conv_w"].data_ptr()), vp(li["conv_state"].data_ptr()), vp(li["conv_state"].data_ptr()),
+            vp(seq["f"].data_ptr()), vp(gp["A_log"].data_ptr()), vp(gp["dt_bias"].data_ptr()),
+            vp(seq["beta_logit"].data_ptr()), ctypes.c_float(-5.0), ctypes.c_float(wl.scale),
+            vp(o.data_ptr()), vp(stream.cuda_stream))
+
+    def launch():
+        rc = lib.kda_prefill_gated(*args)
+        if rc:
+            raise RuntimeError(f"kda_prefill_gated returned {rc}")
+
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            launch()
+        stream.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(steps):
+            launch()
+        e.record(stream)
+        e.synchronize()
+    sec = s.elapsed_time(e) / 1e3 / steps
+    chunks = -(-L // PREFILL_CHUNK)
+    flops = PREFILL_FLOPS_PER_CHUNK_HEAD * chunks * M * H
+    nbytes = (M * (L * PREFILL_TOKEN_BYTES + PREFILL_STREAM_BYTES) + PREFILL_LAYER_BYTES
+              + 2 * wl.state_bytes(state_dtype))
+    del li, gp, seq, o
+    torch.cuda.empty_cache()
+    return {"workload": f"prefill_m{M}_l{L}", "M": M, "L": L, "H": H, "D": D,
+            "state_dtype": state_dtype, "entry_point": "kda_prefill_gated", "launch": "eager",
+            "ms_per_layer": sec * 1e3, "tokens_per_s_per_layer": M * L / sec,
+            "us_per_token_layer": sec * 1e6 / (M * L),
+            "roofline": {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_F32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / sec / 1e12 / MFMA_F32_PEAK_TFLOPS,
+                         "flops_per_launch": flops, "alg_bytes_per_launch": nbytes,
+                         "alg_GBps": nbytes / sec / 1e9}}
 
 
 def stream_ceiling(chunk_bytes, layers, steps, warmup=3):
@@ -413,6 +483,12 @@ def main():
             secondary.append(entry)
             log(f"  {entry['workload']} {sdt} T={T}: {r['launch']} {r['ms_per_layer'] * 1e3:.2f} us/call "
                 f"{r['state_GBps']:.0f} GB/s, algorithmic {r['modes'][r['launch']]['alg_GBps']:.0f} GB/s")
+        for M, L, sdt in PREFILL_SHAPES:
+            r = measure_prefill(M, L, sdt, max(5, args.steps // 20), 2)
+            secondary.append(r)
+            log(f"  {r['workload']} {sdt}: {r['ms_per_layer']:.3f} ms/layer, {r['us_per_token_layer'] * 1e3:.1f} "
+                f"ns/token-layer, {r['roofline']['achieved']:.1f} TFLOP/s ({100 * r['roofline']['frac']:.1f}% "
+                f"of FP32 MFMA), {r['roofline']['alg_GBps']:.0f} GB/s")
 
     ceiling = None
     if not args.no_ceiling:

@@ -6,8 +6,7 @@
 // normalised keys K, scaled queries Q and values V (C-row matrices):
 //
 //   A     = StrictTril(Diag(beta) (Gamma . K) (K / Gamma)^T)
-//   M     = (I + A)^-1 Diag(beta)                      forward substitution
-//   W     = M (Gamma . K),   U = M V
+//   W     = (I + A)^-1 Diag(beta) (Gamma . K),   U = (I + A)^-1 Diag(beta) V
 //   Delta = U - W S
 //   O     = (Gamma . Q) S + Tril((Gamma . Q)(K / Gamma)^T) Delta
 //   S'    = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta
@@ -27,10 +26,29 @@
 // instruction's output layout (row k = 16 mt + 4 (lane / 16) + r, column
 // n = 32 w + 16 nt + lane % 16).  That layout is also a valid B operand for
 // W S and (Gamma . Q) S when the contraction index is enumerated in the same
-// order, so the state is never rearranged.  Per chunk the conv + SiLU, the
-// gate, the norms and the decay products are formed elementwise into LDS,
-// the small C x C products and the 16 x 16 triangular solve run on one or
-// two waves, and the four products with the state run on all four waves.
+// order, so the state is never rearranged.  Per chunk, five phases separated
+// by workgroup barriers:
+//
+//   1. inputs: waves 0, 1, 2 run the conv + SiLU of q, k, v (each lane two
+//      channels over the chunk's 16 tokens, the three previous raw inputs
+//      carried in registers from chunk to chunk) and the L2 norms (one
+//      transposing reduction over the wave for all 16 tokens); wave 3 runs
+//      the forget gate, its running decay product and the write strengths.
+//      The raw inputs of the next chunk are then requested, so their HBM
+//      latency hides behind phases 2 to 5.
+//   2. A (wave 0) and P (wave 1) as 16 x 16 products over the 128 channels;
+//      waves 2 and 3 form Gamma . Q and (gamma_C / Gamma) . K.
+//   3. the triangular solves for W and U, right-looking, one column per
+//      thread (256 columns), straight from (I + A) W = Diag(beta)(Gamma . K).
+//   4. Delta = U - W S and (Gamma . Q) S on all four waves (128 MFMA each).
+//   5. O = (Gamma . Q) S + P Delta, stored; S' (64 MFMA each).
+//
+// LDS rows of the [token][channel] arrays are padded to 132 floats: operand
+// reads with the row chosen by lane % 16 and four consecutive channels per
+// lane (ds_read_b128) and reads with the token chosen by lane / 16 both land
+// on distinct banks.  Where the contraction runs over tokens, the MFMA's k
+// slot lane / 16 stands for tokens 4 (lane / 16) + kk, which keeps those
+// reads conflict-free as well.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,42 +58,72 @@
 
 namespace kda {
 
+
 namespace {
 
 constexpr int PD = 128;            // head width (dk = dv)
 constexpr int PC = 16;             // chunk length, tokens
 constexpr int PNT = 256;           // threads per workgroup (4 waves)
-constexpr int PNG = 3 * PD / 4;    // conv channel groups of 4 per token (q, k, v)
+constexpr int LS = PD + 4;         // LDS row stride of the [token][channel] arrays, floats
+constexpr int LT = PC + 4;         // LDS row stride of the 16 x 16 arrays, floats
 
 struct PrefillSmem {
-    float z[PC][3 * PD];           // conv outputs q | k | v; the q part later holds Delta
-    float G[PC][PD];               // log decays, summed in place; later holds W
-    float GK[PC][PD];              // Gamma . k^
-    float KG[PC][PD];              // k^ / Gamma
-    float GQ[PC][PD];              // Gamma . q^
-    float KT[PC][PD];              // (gamma_C / Gamma) . k^
-    float gam[PD];                 // gamma_C (decay over the whole chunk)
-    float A[PC][PC + 1];
-    float P[PC][PC + 1];
-    float Mx[PC][PC + 1];
-    float beta[PC], rq[PC], rk[PC];
+    float qh[PC][LS];              // q^ (normalised, scaled)
+    float kh[PC][LS];              // k^; after the solve, W
+    float vv[PC][LS];              // v; after the solve, U
+    float eg[PC][LS];              // Gamma (decay from the chunk start); after the state products, Delta
+    float ig[PC][LS];              // 1 / Gamma
+    float gq[PC][LS];              // Gamma . q^
+    float kt[PC][LS];              // (gamma_C / Gamma) . k^
+    float Z[PC][LT];               // Z[j][i] = sum_c (Gamma . k^)[i][c] (k^ / Gamma)[j][c]
+    float P[PC][LT];               // Tril((Gamma . q^)(k^ / Gamma)^T), row = query token
+    float gam[PD];                 // gamma_C, the decay over the whole chunk
+    float beta[PC];
 };
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Raw input (4 bf16 channels at channel offset ch) at sequence position pos
-// of stream m: pos < 0 is a cached tap (tap 3 + pos of conv_in).
-__device__ __forceinline__ u32x2 prefill_input(const Ptrs& p, int L, int m, size_t C3, size_t ch, int pos) {
-    if (pos < 0) return *reinterpret_cast<const u32x2*>(p.conv_in + (size_t)m * 3 * C3 + (size_t)(3 + pos) * C3 + ch);
-    return *reinterpret_cast<const u32x2*>(p.x + ((size_t)m * L + pos) * C3 + ch);
-}
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 __device__ __forceinline__ float load_state_elem(const float* s) { return *s; }
 __device__ __forceinline__ float load_state_elem(const uint16_t* s) { return bf16_lo(*s); }
 __device__ __forceinline__ void store_state_elem(float* s, float v) { *s = v; }
 __device__ __forceinline__ void store_state_elem(uint16_t* s, float v) { *s = (uint16_t)f32_to_bf16_rne(v); }
+
+// Sums over the 64 lanes of a wave for 16 values at once: returns, in every
+// lane, the total of v[lane >> 2].  Each exchange halves the values a lane
+// carries (lane bit 5 picks tokens 8..15, bit 4 the upper four of those, ...),
+// 17 exchanges instead of 16 x 6.
+__device__ __forceinline__ float wave_sum16(const float (&v)[PC], int lane) {
+    float a8[8], a4[4], a2[2];
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float keep = b5 ? v[k + 8] : v[k], send = b5 ? v[k] : v[k + 8];
+        a8[k] = keep + __shfl_xor(send, 32, 64);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float keep = b4 ? a8[k + 4] : a8[k], send = b4 ? a8[k] : a8[k + 4];
+        a4[k] = keep + __shfl_xor(send, 16, 64);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float keep = b3 ? a4[k + 2] : a4[k], send = b3 ? a4[k] : a4[k + 2];
+        a2[k] = keep + __shfl_xor(send, 8, 64);
+    }
+    const bool b2 = lane & 4;
+    float t = (b2 ? a2[1] : a2[0]) + __shfl_xor(b2 ? a2[0] : a2[1], 4, 64);
+    t += __shfl_xor(t, 2, 64);
+    t += __shfl_xor(t, 1, 64);
+    return t;
+}
+
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
 
 }  // namespace
 
@@ -88,7 +136,8 @@ void prefill_kernel(const Ptrs p, const int L)
     __shared__ PrefillSmem sm;
     const int unit = (int)blockIdx.x;
     const int m = unit / p.H, h = unit - m * p.H;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform: roles branch on it
     const int l16 = lane & 15, g4 = lane >> 4;
     const size_t HD = (size_t)p.H * PD, C3 = 3 * HD;
     const int ncol = 32 * wv;                          // this wave's value columns
@@ -104,206 +153,260 @@ void prefill_kernel(const Ptrs p, const int L)
             for (int r = 0; r < 4; ++r)
                 S[mt][nt][r] = load_state_elem(st + (size_t)(16 * mt + 4 * g4 + r) * PD + ncol + 16 * nt + l16);
 
+    // ---- per-lane constants of the input phase ----
+    // waves 0..2: channels 2 lane, 2 lane + 1 of q, k or v (tensor wv)
+    const size_t ch = (size_t)(wv < 3 ? wv : 0) * HD + (size_t)h * PD + 2 * lane;
+    float cw[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    uint32_t h0 = 0, h1 = 0, h2 = 0;                   // raw inputs of the 3 previous tokens
+    // wave 3: forget gate of channels 2 lane, 2 lane + 1
+    float db0 = 0.f, db1 = 0.f;
     const float eA = expf(p.A_log[h]);
     const float lb = p.lower_bound;
+    if (wv < 3) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
+        cw[0] = bf16_lo(w.x); cw[1] = bf16_hi(w.x); cw[2] = bf16_lo(w.y); cw[3] = bf16_hi(w.y);
+        cw[4] = bf16_lo(w.z); cw[5] = bf16_hi(w.z); cw[6] = bf16_lo(w.w); cw[7] = bf16_hi(w.w);
+        const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
+        h0 = *reinterpret_cast<const uint32_t*>(ci);
+        h1 = *reinterpret_cast<const uint32_t*>(ci + C3);
+        h2 = *reinterpret_cast<const uint32_t*>(ci + 2 * C3);
+    } else {
+        db0 = p.dt_bias[(size_t)h * PD + 2 * lane];
+        db1 = p.dt_bias[(size_t)h * PD + 2 * lane + 1];
+    }
+
+    // raw inputs of one chunk: waves 0..2 x (2 bf16 per token), wave 3 the
+    // forget-gate projection (2 bf16 per token) and, lanes 0..15, the
+    // write-strength logit of token `lane`.  Past the end of the sequence
+    // the last token is read again; its results are masked out.
+    uint32_t raw[PC];
+    uint32_t rawb = 0;
+    auto fetch = [&](int t0) {
+        const int last = min(PC, L - t0) - 1;
+        if (wv < 3) {
+            const uint16_t* xp = p.x + ((size_t)m * L + t0) * C3 + ch;
+#pragma unroll
+            for (int j = 0; j < PC; ++j)
+                raw[j] = *reinterpret_cast<const uint32_t*>(xp + (size_t)min(j, last) * C3);
+        } else {
+            const uint16_t* fp = p.fgate + ((size_t)m * L + t0) * HD + (size_t)h * PD + 2 * lane;
+#pragma unroll
+            for (int j = 0; j < PC; ++j)
+                raw[j] = *reinterpret_cast<const uint32_t*>(fp + (size_t)min(j, last) * HD);
+            rawb = p.blogit[((size_t)m * L + t0 + min(lane & (PC - 1), last)) * p.H + h];
+        }
+    };
+    fetch(0);
 
     for (int t0 = 0; t0 < L; t0 += PC) {
         const int n = min(PC, L - t0);
 
-        // ---- conv + SiLU of the chunk's tokens (q, k, v), 4 channels per item ----
-        for (int idx = tid; idx < PC * PNG; idx += PNT) {
-            const int j = idx / PNG, g = idx - j * PNG;
-            f32x4 zv = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (j < n) {
-                const int tok = t0 + j;
-                const int tensor = g / (PD / 4);
-                const size_t ch = (size_t)tensor * HD + (size_t)h * PD + 4 * (g - tensor * (PD / 4));
-                const u32x2 xv = prefill_input(p, L, m, C3, ch, tok);
-                const u32x2 t2 = prefill_input(p, L, m, C3, ch, tok - 1);
-                const u32x2 t1 = prefill_input(p, L, m, C3, ch, tok - 2);
-                const u32x2 t0v = prefill_input(p, L, m, C3, ch, tok - 3);
-                const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
-                const u32x4 w01 = wp[0], w23 = wp[1];
-                zv = f32x4{conv_silu(u32x2{w01.x, w01.y}, bf16_lo(t0v.x), bf16_lo(t1.x), bf16_lo(t2.x), bf16_lo(xv.x)),
-                           conv_silu(u32x2{w01.z, w01.w}, bf16_hi(t0v.x), bf16_hi(t1.x), bf16_hi(t2.x), bf16_hi(xv.x)),
-                           conv_silu(u32x2{w23.x, w23.y}, bf16_lo(t0v.y), bf16_lo(t1.y), bf16_lo(t2.y), bf16_lo(xv.y)),
-                           conv_silu(u32x2{w23.z, w23.w}, bf16_hi(t0v.y), bf16_hi(t1.y), bf16_hi(t2.y), bf16_hi(xv.y))};
-            }
-            reinterpret_cast<f32x4*>(sm.z[j])[g] = zv;
-        }
-        // forget gate in log space, g = lb * sigmoid(exp(A) (f + b)) (0 past the end)
-        for (int idx = tid; idx < PC * (PD / 4); idx += PNT) {
-            const int j = idx / (PD / 4), q = idx - j * (PD / 4);
-            f32x4 gl = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (j < n) {
-                const u32x2 fv = *reinterpret_cast<const u32x2*>(
-                    p.fgate + ((size_t)m * L + t0 + j) * HD + (size_t)h * PD + 4 * q);
-                const f32x4 bv = *reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)h * PD + 4 * q);
-                gl = f32x4{lb / (1.0f + expf(-eA * (bf16_lo(fv.x) + bv.x))),
-                           lb / (1.0f + expf(-eA * (bf16_hi(fv.x) + bv.y))),
-                           lb / (1.0f + expf(-eA * (bf16_lo(fv.y) + bv.z))),
-                           lb / (1.0f + expf(-eA * (bf16_hi(fv.y) + bv.w)))};
-            }
-            reinterpret_cast<f32x4*>(sm.G[j])[q] = gl;
-        }
-        if (tid < PC) {
-            sm.beta[tid] = tid < n
-                ? 1.0f / (1.0f + expf(-bf16_lo(p.blogit[((size_t)m * L + t0 + tid) * p.H + h])))
-                : 0.0f;
-        }
-        lds_barrier();
-
-        // ---- norms (one wave per token) and cumulative decays (one thread per channel) ----
-        for (int j = wv; j < PC; j += PNT / 64) {
-            float sqq = 0.0f, skk = 0.0f;
-#pragma unroll
-            for (int i = lane; i < PD; i += 64) {
-                const float qv = sm.z[j][i], kv = sm.z[j][PD + i];
-                sqq = fmaf(qv, qv, sqq);
-                skk = fmaf(kv, kv, skk);
-            }
-            sqq = wave_sum(sqq);
-            skk = wave_sum(skk);
-            if (lane == 0) {
-                sm.rq[j] = j < n ? p.scale * rsqrtf(sqq + 1e-6f) : 0.0f;
-                sm.rk[j] = j < n ? rsqrtf(skk + 1e-6f) : 0.0f;
-            }
-        }
-        if (tid < PD) {
-            float acc = 0.0f;
+        // ---- 1. inputs ----
+        if (wv < 3) {
+            // tokens past the end give 0 (the carried taps are then stale,
+            // but only the last chunk has such tokens)
+            float z0[PC], z1[PC];
 #pragma unroll
             for (int j = 0; j < PC; ++j) {
-                acc += sm.G[j][tid];
-                sm.G[j][tid] = acc;
+                const uint32_t xv = raw[j];
+                float y0 = cw[0] * bf16_lo(h0);
+                y0 = fmaf(cw[1], bf16_lo(h1), y0);
+                y0 = fmaf(cw[2], bf16_lo(h2), y0);
+                y0 = fmaf(cw[3], bf16_lo(xv), y0);
+                float y1 = cw[4] * bf16_hi(h0);
+                y1 = fmaf(cw[5], bf16_hi(h1), y1);
+                y1 = fmaf(cw[6], bf16_hi(h2), y1);
+                y1 = fmaf(cw[7], bf16_hi(xv), y1);
+                // SiLU with the hardware reciprocal (within 3.6 ulp)
+                z0[j] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
+                z1[j] = j < n ? y1 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y1)) : 0.f;
+                h0 = h1;
+                h1 = h2;
+                h2 = xv;
             }
-            sm.gam[tid] = expf(acc);
+            if (t0 + PC < L) fetch(t0 + PC);
+            float (*dst)[LS] = wv == 0 ? sm.qh : wv == 1 ? sm.kh : sm.vv;
+            if (wv < 2) {
+                float ss[PC];
+#pragma unroll
+                for (int j = 0; j < PC; ++j) ss[j] = fmaf(z0[j], z0[j], z1[j] * z1[j]);
+                const float tot = wave_sum16(ss, lane);
+                const float rn = (wv == 0 ? p.scale : 1.0f) * rsqrtf(tot + 1e-6f);
+#pragma unroll
+                for (int j = 0; j < PC; ++j) {
+                    const float rj = lane_value(rn, 4 * j);
+                    z0[j] *= rj;
+                    z1[j] *= rj;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PC; ++j)
+                *reinterpret_cast<float2*>(&dst[j][2 * lane]) = make_float2(z0[j], z1[j]);
+        } else {
+            // g = lb * sigmoid(exp(A) (f + b)), alpha = e^g; Gamma_j is the
+            // running product of alpha from the chunk start (the decay the
+            // per-token recurrence applies between the chunk start and j)
+            float e0 = 1.f, e1 = 1.f;
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+                const float g0 = lb * __builtin_amdgcn_rcpf(1.0f + exp_fast(-eA * (bf16_lo(raw[j]) + db0)));
+                const float g1 = lb * __builtin_amdgcn_rcpf(1.0f + exp_fast(-eA * (bf16_hi(raw[j]) + db1)));
+                e0 *= j < n ? exp_fast(g0) : 1.f;
+                e1 *= j < n ? exp_fast(g1) : 1.f;
+                *reinterpret_cast<float2*>(&sm.eg[j][2 * lane]) = make_float2(e0, e1);
+                *reinterpret_cast<float2*>(&sm.ig[j][2 * lane]) =
+                    make_float2(__builtin_amdgcn_rcpf(e0), __builtin_amdgcn_rcpf(e1));
+            }
+            *reinterpret_cast<float2*>(&sm.gam[2 * lane]) = make_float2(e0, e1);
+            if (lane < PC)
+                sm.beta[lane] = lane < n ? __builtin_amdgcn_rcpf(1.0f + exp_fast(-bf16_lo(rawb))) : 0.0f;
+            if (t0 + PC < L) fetch(t0 + PC);
         }
         lds_barrier();
 
-        // ---- decay-weighted keys and queries ----
-        for (int e = tid; e < PC * PD; e += PNT) {
-            const int j = e / PD, c = e - j * PD;
-            const float Gj = sm.G[j][c];
-            const float kh = sm.z[j][PD + c] * sm.rk[j], qh = sm.z[j][c] * sm.rq[j];
-            const float eg = expf(Gj), ig = expf(-Gj);
-            sm.GK[j][c] = kh * eg;
-            sm.KG[j][c] = kh * ig;
-            sm.GQ[j][c] = qh * eg;
-            sm.KT[j][c] = kh * expf(sm.G[PC - 1][c] - Gj);
-        }
-        lds_barrier();
-
-        // ---- A (wave 0) and P (wave 1): 16 x 16 products over the 128 channels ----
+        // ---- 2. A and P over the channels (waves 0, 1); Gamma . q^ and (gamma_C / Gamma) . k^ ----
         if (wv < 2) {
-            const float (*X)[PD] = wv == 0 ? sm.GK : sm.GQ;
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-            for (int kk = 0; kk < PD / 4; ++kk)
-                acc = mfma16(X[l16][4 * kk + g4], sm.KG[l16][4 * kk + g4], acc);
+            // lane / 16 takes channels [32 (lane / 16), 32 (lane / 16) + 32)
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r, s = l16;
-                if (wv == 0) sm.A[t][s] = s < t ? sm.beta[t] * acc[r] : 0.0f;
-                else sm.P[t][s] = s <= t ? acc[r] : 0.0f;
+            for (int q = 0; q < 8; ++q) {
+                const int c = 32 * g4 + 4 * q;
+                const f32x4 k4 = lds4(&sm.kh[l16][c]), e4 = lds4(&sm.eg[l16][c]), i4 = lds4(&sm.ig[l16][c]);
+                if (wv == 0) {
+                    // D[i][j] = sum_c (Gamma k^)[i][c] (k^ / Gamma)[j][c] = Z[j][i]
+                    acc0 = mfma16(k4.x * e4.x, k4.x * i4.x, acc0);
+                    acc1 = mfma16(k4.y * e4.y, k4.y * i4.y, acc1);
+                    acc0 = mfma16(k4.z * e4.z, k4.z * i4.z, acc0);
+                    acc1 = mfma16(k4.w * e4.w, k4.w * i4.w, acc1);
+                } else {
+                    // D[s][t] = sum_c (k^ / Gamma)[s][c] (Gamma q^)[t][c] = P[t][s]
+                    const f32x4 q4 = lds4(&sm.qh[l16][c]);
+                    acc0 = mfma16(k4.x * i4.x, q4.x * e4.x, acc0);
+                    acc1 = mfma16(k4.y * i4.y, q4.y * e4.y, acc1);
+                    acc0 = mfma16(k4.z * i4.z, q4.z * e4.z, acc0);
+                    acc1 = mfma16(k4.w * i4.w, q4.w * e4.w, acc1);
+                }
+            }
+            f32x4 d = acc0 + acc1;
+            if (wv == 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g4 + r > l16) d[r] = 0.f;     // keep s <= t
+                *reinterpret_cast<f32x4*>(&sm.P[l16][4 * g4]) = d;
+            } else {
+                *reinterpret_cast<f32x4*>(&sm.Z[l16][4 * g4]) = d;
+            }
+        } else {
+            for (int e = tid - 128; e < PC * (PD / 4); e += 128) {
+                const int j = e >> 5, c = 4 * (e & 31);
+                const f32x4 q4 = lds4(&sm.qh[j][c]), e4 = lds4(&sm.eg[j][c]);
+                const f32x4 k4 = lds4(&sm.kh[j][c]), i4 = lds4(&sm.ig[j][c]), gm = lds4(&sm.gam[c]);
+                *reinterpret_cast<f32x4*>(&sm.gq[j][c]) = q4 * e4;
+                *reinterpret_cast<f32x4*>(&sm.kt[j][c]) = k4 * (gm * i4);
             }
         }
         lds_barrier();
 
-        // ---- M = (I + A)^-1 Diag(beta): forward substitution, one column per lane ----
-        if (tid < PC) {
-            const int c = tid;
-            float x[PC];
+        // ---- 3. (I + A) W = Diag(beta)(Gamma . K), (I + A) U = Diag(beta) V ----
+        // Right-looking: c_i holds the right-hand side minus the columns
+        // already solved; x_j = beta_j c_j once every earlier column is in.
+        {
+            const int col = tid & (PD - 1);
+            float (*X)[LS] = wv < 2 ? sm.kh : sm.vv;
+            float cv[PC];
+            if (wv < 2) {
 #pragma unroll
-            for (int i = 0; i < PC; ++i) {
-                float v = i == c ? sm.beta[i] : 0.0f;
+                for (int j = 0; j < PC; ++j) cv[j] = sm.kh[j][col] * sm.eg[j][col];
+            } else {
 #pragma unroll
-                for (int j = 0; j < i; ++j) v = fmaf(-sm.A[i][j], x[j], v);
-                x[i] = v;
-                sm.Mx[i][c] = v;
+                for (int j = 0; j < PC; ++j) cv[j] = sm.vv[j][col];
             }
+            const f32x4 b0 = lds4(&sm.beta[0]), b1 = lds4(&sm.beta[4]), b2 = lds4(&sm.beta[8]), b3 = lds4(&sm.beta[12]);
+            const float bt[PC] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w,
+                                  b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+                const float xj = bt[j] * cv[j];
+                cv[j] = xj;
+#pragma unroll
+                for (int q = (j + 1) / 4; q < PC / 4; ++q) {
+                    const f32x4 z = lds4(&sm.Z[j][4 * q]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * q + r > j) cv[4 * q + r] = fmaf(-z[r], xj, cv[4 * q + r]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PC; ++j) X[j][col] = cv[j];
         }
         lds_barrier();
 
-        // ---- W = M (Gamma . K) into LDS (G's storage), U = M V in registers ----
-        f32x4 U[2], Wr[2];
+        // ---- 4. Delta = U - W S and (Gamma . Q) S, this wave's 32 value columns ----
+        f32x4 dacc[2], oacc[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            f32x4 aw = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
-            const int col = ncol + 16 * nt + l16;
 #pragma unroll
-            for (int kk = 0; kk < PC / 4; ++kk) {
-                const float a = sm.Mx[l16][4 * kk + g4];
-                aw = mfma16(a, sm.GK[4 * kk + g4][col], aw);
-                au = mfma16(a, sm.z[4 * kk + g4][2 * PD + col], au);
-            }
-            Wr[nt] = aw;
-            U[nt] = au;
+            for (int r = 0; r < 4; ++r) dacc[nt][r] = sm.vv[4 * g4 + r][ncol + 16 * nt + l16];
+            oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        // W replaces the cumulative decays, which nobody reads any more
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.G[4 * g4 + r][ncol + 16 * nt + l16] = Wr[nt][r];
-        lds_barrier();
-
-        // ---- Delta = U - W S and (Gamma . Q) S, this wave's 32 value columns ----
-        f32x4 dacc[2] = {U[0], U[1]};
-        f32x4 oacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
+            const f32x4 w4 = lds4(&sm.kh[l16][16 * mt + 4 * g4]);
+            const f32x4 q4 = lds4(&sm.gq[l16][16 * mt + 4 * g4]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int k = 16 * mt + 4 * g4 + r;
-                const float aw = -sm.G[l16][k], aq = sm.GQ[l16][k];
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    dacc[nt] = mfma16(aw, S[mt][nt][r], dacc[nt]);
-                    oacc[nt] = mfma16(aq, S[mt][nt][r], oacc[nt]);
+                    dacc[nt] = mfma16(-w4[r], S[mt][nt][r], dacc[nt]);
+                    oacc[nt] = mfma16(q4[r], S[mt][nt][r], oacc[nt]);
                 }
             }
         }
-        // Delta replaces the conv q outputs, which nobody reads any more
+        // Delta replaces Gamma, which nobody reads any more
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.z[4 * g4 + r][ncol + 16 * nt + l16] = dacc[nt][r];
+            for (int r = 0; r < 4; ++r) sm.eg[4 * g4 + r][ncol + 16 * nt + l16] = dacc[nt][r];
         lds_barrier();
 
-        // ---- O = (Gamma . Q) S + P Delta ----
+        // ---- 5. O = (Gamma . Q) S + P Delta; S' = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta ----
+        // contraction over tokens: the k slot lane / 16 is token 4 (lane / 16) + kk
+        float dl[2][4];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int col = ncol + 16 * nt + l16;
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int kk = 0; kk < PC / 4; ++kk)
-                oacc[nt] = mfma16(sm.P[l16][4 * kk + g4], sm.z[4 * kk + g4][col], oacc[nt]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
-                if (t < n)
-                    p.o[(((size_t)m * L + t0 + t) * p.H + h) * PD + col] = (uint16_t)f32_to_bf16_rne(oacc[nt][r]);
-            }
-        }
-
-        // ---- S' = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta ----
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float gk = sm.gam[16 * mt + 4 * g4 + r];
-                S[mt][0][r] *= gk;
-                S[mt][1][r] *= gk;
-            }
+            for (int kk = 0; kk < 4; ++kk) dl[nt][kk] = sm.eg[4 * g4 + kk][ncol + 16 * nt + l16];
+        {
+            const f32x4 p4 = lds4(&sm.P[l16][4 * g4]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                f32x4 acc = {S[mt][nt][0], S[mt][nt][1], S[mt][nt][2], S[mt][nt][3]};
 #pragma unroll
-                for (int kk = 0; kk < PC / 4; ++kk)
-                    acc = mfma16(sm.KT[4 * kk + g4][16 * mt + l16], sm.z[4 * kk + g4][ncol + 16 * nt + l16], acc);
+                for (int kk = 0; kk < 4; ++kk) oacc[nt] = mfma16(p4[kk], dl[nt][kk], oacc[nt]);
+                const int col = ncol + 16 * nt + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * g4 + r;
+                    if (t < n)
+                        p.o[(((size_t)m * L + t0 + t) * p.H + h) * PD + col] = (uint16_t)f32_to_bf16_rne(oacc[nt][r]);
+                }
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const f32x4 gm = lds4(&sm.gam[16 * mt + 4 * g4]);
+            float a[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) a[kk] = sm.kt[4 * g4 + kk][16 * mt + l16];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x4 acc = {S[mt][nt][0] * gm.x, S[mt][nt][1] * gm.y, S[mt][nt][2] * gm.z, S[mt][nt][3] * gm.w};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mfma16(a[kk], dl[nt][kk], acc);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[mt][nt][r] = acc[r];
             }
         }
-        // the next chunk overwrites every vector above
+        // the next chunk's inputs overwrite every array above
         lds_barrier();
     }
 
@@ -314,18 +417,20 @@ void prefill_kernel(const Ptrs p, const int L)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 store_state_elem(st + (size_t)(16 * mt + 4 * g4 + r) * PD + ncol + 16 * nt + l16, S[mt][nt][r]);
-    // conv state after the sequence: positions L-3, L-2, L-1 (a position < 0
-    // is a cached tap, read before it is overwritten)
-    if (tid < PNG) {
-        const int tensor = tid / (PD / 4);
-        const size_t ch = (size_t)tensor * HD + (size_t)h * PD + 4 * (tid - tensor * (PD / 4));
-        const u32x2 n0 = prefill_input(p, L, m, C3, ch, L - 3);
-        const u32x2 n1 = prefill_input(p, L, m, C3, ch, L - 2);
-        const u32x2 n2 = prefill_input(p, L, m, C3, ch, L - 1);
+    // conv state after the sequence: the raw inputs of positions L-3, L-2,
+    // L-1, where a position < 0 is a cached tap (read before this lane
+    // overwrites it: conv_out may be conv_in, and each lane owns its channels)
+    if (wv < 3) {
+        uint32_t nt3[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int pos = L - 3 + k;
+            nt3[k] = pos < 0 ? *reinterpret_cast<const uint32_t*>(p.conv_in + (size_t)m * 3 * C3 + (size_t)(3 + pos) * C3 + ch)
+                             : *reinterpret_cast<const uint32_t*>(p.x + ((size_t)m * L + pos) * C3 + ch);
+        }
         uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + ch;
-        *reinterpret_cast<u32x2*>(co) = n0;
-        *reinterpret_cast<u32x2*>(co + C3) = n1;
-        *reinterpret_cast<u32x2*>(co + 2 * C3) = n2;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) *reinterpret_cast<uint32_t*>(co + (size_t)k * C3) = nt3[k];
     }
 }
 

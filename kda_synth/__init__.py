@@ -34,6 +34,10 @@ not available; these put the keep factor mostly in (0.6, 0.99)):
 * write-strength logits ~ N(0, 1), BF16, per token;
 * output gate ~ N(0, 1), BF16, per token; RMSNorm weight 1 + 0.1 N(0, 1),
   FP32, fixed per layer.
+
+Whole sequences for the chunked prefill (``sequence_inputs``) draw the same
+distributions once per tensor for all L tokens (one generator each), so a
+long prompt costs one draw instead of L.
 """
 from __future__ import annotations
 
@@ -195,3 +199,13 @@ def gate_inputs(wl: Workload, layer: int, step: int, device) -> dict:
     bl = _randn((M, H), _gen(wl, layer, step, "beta_logit", device), device).to(BF16)
     og = _randn((M, H * D), _gen(wl, layer, step, "out_gate", device), device).to(BF16)
     return {"f": f, "beta_logit": bl, "out_gate": og}
+
+
+def sequence_inputs(wl: Workload, layer: int, L: int, device) -> dict:
+    """L tokens at once for the chunked prefill: x [M,L,3,H*D], f [M,L,H*D],
+    beta_logit [M,L,H], all BF16, the per-token distributions."""
+    M, H, D = wl.M, wl.H, wl.D
+    x = _randn((M, L, 3, H * D), _gen(wl, layer, -1, "seq_x", device), device).to(BF16)
+    f = _randn((M, L, H * D), _gen(wl, layer, -1, "seq_f_gate", device), device).to(BF16)
+    bl = _randn((M, L, H), _gen(wl, layer, -1, "seq_beta_logit", device), device).to(BF16)
+    return {"x": x, "f": f, "beta_logit": bl}
