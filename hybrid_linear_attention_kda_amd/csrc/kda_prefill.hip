@@ -37,10 +37,11 @@
 //      The raw inputs of the next chunk are then requested, so their HBM
 //      latency hides behind phases 2 to 5.
 //   2. A (wave 0) and P (wave 1) as 16 x 16 products over the 128 channels;
-//      waves 2 and 3 form Gamma . Q and (gamma_C / Gamma) . K.
+//      waves 2 and 3 form (gamma_C / Gamma) . K.
 //   3. the triangular solves for W and U, right-looking, one column per
-//      thread (256 columns), straight from (I + A) W = Diag(beta)(Gamma . K).
-//   4. Delta = U - W S and (Gamma . Q) S on all four waves (128 MFMA each).
+//      thread (256 columns), straight from (I + A) W = Diag(beta)(Gamma . K),
+//      while the matrix cores form (Gamma . Q) S (64 MFMA per wave).
+//   4. Delta = U - W S on all four waves (64 MFMA each).
 //   5. O = (Gamma . Q) S + P Delta, stored; S' (64 MFMA each).
 //
 // LDS rows of the [token][channel] arrays are padded to 132 floats: operand
@@ -69,11 +70,10 @@ constexpr int LT = PC + 4;         // LDS row stride of the 16 x 16 arrays, floa
 
 struct PrefillSmem {
     float qh[PC][LS];              // q^ (normalised, scaled)
-    float kh[PC][LS];              // k^; after the solve, W
+    float kh[PC][LS];              // k^; after the solve, -W
     float vv[PC][LS];              // v; after the solve, U
     float eg[PC][LS];              // Gamma (decay from the chunk start); after the state products, Delta
     float ig[PC][LS];              // 1 / Gamma
-    float gq[PC][LS];              // Gamma . q^
     float kt[PC][LS];              // (gamma_C / Gamma) . k^
     float Z[PC][LT];               // Z[j][i] = sum_c (Gamma . k^)[i][c] (k^ / Gamma)[j][c]
     float P[PC][LT];               // Tril((Gamma . q^)(k^ / Gamma)^T), row = query token
@@ -130,7 +130,7 @@ __device__ __forceinline__ float lane_value(float v, int src) {
 // One workgroup per (stream, head); x [M][L][3][H*D], fgate [M][L][H*D],
 // blogit [M][L][H], o [M][L][H][D].
 template <typename TS>
-__global__ __launch_bounds__(PNT)
+__global__ __launch_bounds__(PNT, 2)
 void prefill_kernel(const Ptrs p, const int L)
 {
     __shared__ PrefillSmem sm;
@@ -157,7 +157,8 @@ void prefill_kernel(const Ptrs p, const int L)
     // waves 0..2: channels 2 lane, 2 lane + 1 of q, k or v (tensor wv)
     const size_t ch = (size_t)(wv < 3 ? wv : 0) * HD + (size_t)h * PD + 2 * lane;
     float cw[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    uint32_t h0 = 0, h1 = 0, h2 = 0;                   // raw inputs of the 3 previous tokens
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f;                // raw inputs of the 3 previous tokens, channel 2 lane
+    float b0 = 0.f, b1 = 0.f, b2 = 0.f;                // the same, channel 2 lane + 1
     // wave 3: forget gate of channels 2 lane, 2 lane + 1
     float db0 = 0.f, db1 = 0.f;
     const float eA = expf(p.A_log[h]);
@@ -167,9 +168,11 @@ void prefill_kernel(const Ptrs p, const int L)
         cw[0] = bf16_lo(w.x); cw[1] = bf16_hi(w.x); cw[2] = bf16_lo(w.y); cw[3] = bf16_hi(w.y);
         cw[4] = bf16_lo(w.z); cw[5] = bf16_hi(w.z); cw[6] = bf16_lo(w.w); cw[7] = bf16_hi(w.w);
         const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
-        h0 = *reinterpret_cast<const uint32_t*>(ci);
-        h1 = *reinterpret_cast<const uint32_t*>(ci + C3);
-        h2 = *reinterpret_cast<const uint32_t*>(ci + 2 * C3);
+        const uint32_t t0v = *reinterpret_cast<const uint32_t*>(ci);
+        const uint32_t t1v = *reinterpret_cast<const uint32_t*>(ci + C3);
+        const uint32_t t2v = *reinterpret_cast<const uint32_t*>(ci + 2 * C3);
+        a0 = bf16_lo(t0v); a1 = bf16_lo(t1v); a2 = bf16_lo(t2v);
+        b0 = bf16_hi(t0v); b1 = bf16_hi(t1v); b2 = bf16_hi(t2v);
     } else {
         db0 = p.dt_bias[(size_t)h * PD + 2 * lane];
         db1 = p.dt_bias[(size_t)h * PD + 2 * lane + 1];
@@ -208,21 +211,20 @@ void prefill_kernel(const Ptrs p, const int L)
             float z0[PC], z1[PC];
 #pragma unroll
             for (int j = 0; j < PC; ++j) {
-                const uint32_t xv = raw[j];
-                float y0 = cw[0] * bf16_lo(h0);
-                y0 = fmaf(cw[1], bf16_lo(h1), y0);
-                y0 = fmaf(cw[2], bf16_lo(h2), y0);
-                y0 = fmaf(cw[3], bf16_lo(xv), y0);
-                float y1 = cw[4] * bf16_hi(h0);
-                y1 = fmaf(cw[5], bf16_hi(h1), y1);
-                y1 = fmaf(cw[6], bf16_hi(h2), y1);
-                y1 = fmaf(cw[7], bf16_hi(xv), y1);
+                const float x0 = bf16_lo(raw[j]), x1 = bf16_hi(raw[j]);
+                float y0 = cw[0] * a0;
+                y0 = fmaf(cw[1], a1, y0);
+                y0 = fmaf(cw[2], a2, y0);
+                y0 = fmaf(cw[3], x0, y0);
+                float y1 = cw[4] * b0;
+                y1 = fmaf(cw[5], b1, y1);
+                y1 = fmaf(cw[6], b2, y1);
+                y1 = fmaf(cw[7], x1, y1);
                 // SiLU with the hardware reciprocal (within 3.6 ulp)
                 z0[j] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
                 z1[j] = j < n ? y1 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y1)) : 0.f;
-                h0 = h1;
-                h1 = h2;
-                h2 = xv;
+                a0 = a1; a1 = a2; a2 = x0;
+                b0 = b1; b1 = b2; b2 = x1;
             }
             if (t0 + PC < L) fetch(t0 + PC);
             float (*dst)[LS] = wv == 0 ? sm.qh : wv == 1 ? sm.kh : sm.vv;
@@ -264,7 +266,7 @@ void prefill_kernel(const Ptrs p, const int L)
         }
         lds_barrier();
 
-        // ---- 2. A and P over the channels (waves 0, 1); Gamma . q^ and (gamma_C / Gamma) . k^ ----
+        // ---- 2. A and P over the channels (waves 0, 1); (gamma_C / Gamma) . k^ (waves 2, 3) ----
         if (wv < 2) {
             // lane / 16 takes channels [32 (lane / 16), 32 (lane / 16) + 32)
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -299,31 +301,40 @@ void prefill_kernel(const Ptrs p, const int L)
         } else {
             for (int e = tid - 128; e < PC * (PD / 4); e += 128) {
                 const int j = e >> 5, c = 4 * (e & 31);
-                const f32x4 q4 = lds4(&sm.qh[j][c]), e4 = lds4(&sm.eg[j][c]);
                 const f32x4 k4 = lds4(&sm.kh[j][c]), i4 = lds4(&sm.ig[j][c]), gm = lds4(&sm.gam[c]);
-                *reinterpret_cast<f32x4*>(&sm.gq[j][c]) = q4 * e4;
                 *reinterpret_cast<f32x4*>(&sm.kt[j][c]) = k4 * (gm * i4);
             }
         }
         lds_barrier();
 
-        // ---- 3. (I + A) W = Diag(beta)(Gamma . K), (I + A) U = Diag(beta) V ----
+        // ---- 3. (I + A) W = Diag(beta)(Gamma . K), (I + A) U = Diag(beta) V; (Gamma . Q) S ----
         // Right-looking: c_i holds the right-hand side minus the columns
         // already solved; x_j = beta_j c_j once every earlier column is in.
+        // Waves 0, 1 solve for W (stored negated), waves 2, 3 for U.  The
+        // matrix cores meanwhile form (Gamma . Q) S for this wave's columns,
+        // Gamma . q^ made on the fly; the two are independent, so one block
+        // lets the scheduler interleave them.
+        f32x4 oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         {
+            const bool isw = wv < 2;
             const int col = tid & (PD - 1);
-            float (*X)[LS] = wv < 2 ? sm.kh : sm.vv;
+            float (*X)[LS] = isw ? sm.kh : sm.vv;
             float cv[PC];
-            if (wv < 2) {
 #pragma unroll
-                for (int j = 0; j < PC; ++j) cv[j] = sm.kh[j][col] * sm.eg[j][col];
-            } else {
+            for (int j = 0; j < PC; ++j) cv[j] = X[j][col] * (isw ? sm.eg[j][col] : 1.0f);
+            const f32x4 bb0 = lds4(&sm.beta[0]), bb1 = lds4(&sm.beta[4]), bb2 = lds4(&sm.beta[8]), bb3 = lds4(&sm.beta[12]);
+            const float bt[PC] = {bb0.x, bb0.y, bb0.z, bb0.w, bb1.x, bb1.y, bb1.z, bb1.w,
+                                  bb2.x, bb2.y, bb2.z, bb2.w, bb3.x, bb3.y, bb3.z, bb3.w};
 #pragma unroll
-                for (int j = 0; j < PC; ++j) cv[j] = sm.vv[j][col];
+            for (int mt = 0; mt < 8; ++mt) {
+                const f32x4 q4 = lds4(&sm.qh[l16][16 * mt + 4 * g4]), e4 = lds4(&sm.eg[l16][16 * mt + 4 * g4]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a = q4[r] * e4[r];
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) oacc[nt] = mfma16(a, S[mt][nt][r], oacc[nt]);
+                }
             }
-            const f32x4 b0 = lds4(&sm.beta[0]), b1 = lds4(&sm.beta[4]), b2 = lds4(&sm.beta[8]), b3 = lds4(&sm.beta[12]);
-            const float bt[PC] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w,
-                                  b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
 #pragma unroll
             for (int j = 0; j < PC; ++j) {
                 const float xj = bt[j] * cv[j];
@@ -336,31 +347,25 @@ void prefill_kernel(const Ptrs p, const int L)
                         if (4 * q + r > j) cv[4 * q + r] = fmaf(-z[r], xj, cv[4 * q + r]);
                 }
             }
+            // each thread reads and overwrites only its own column of k^ or v
 #pragma unroll
-            for (int j = 0; j < PC; ++j) X[j][col] = cv[j];
+            for (int j = 0; j < PC; ++j) X[j][col] = isw ? -cv[j] : cv[j];
         }
         lds_barrier();
 
-        // ---- 4. Delta = U - W S and (Gamma . Q) S, this wave's 32 value columns ----
-        f32x4 dacc[2], oacc[2];
+        // ---- 4. Delta = U - W S, this wave's 32 value columns ----
+        f32x4 dacc[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) dacc[nt][r] = sm.vv[4 * g4 + r][ncol + 16 * nt + l16];
-            oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            const f32x4 w4 = lds4(&sm.kh[l16][16 * mt + 4 * g4]);
-            const f32x4 q4 = lds4(&sm.gq[l16][16 * mt + 4 * g4]);
+            const f32x4 w4 = lds4(&sm.kh[l16][16 * mt + 4 * g4]);   // -W
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    dacc[nt] = mfma16(-w4[r], S[mt][nt][r], dacc[nt]);
-                    oacc[nt] = mfma16(q4[r], S[mt][nt][r], oacc[nt]);
-                }
-            }
+                for (int nt = 0; nt < 2; ++nt) dacc[nt] = mfma16(w4[r], S[mt][nt][r], dacc[nt]);
         }
         // Delta replaces Gamma, which nobody reads any more
 #pragma unroll
@@ -410,13 +415,17 @@ void prefill_kernel(const Ptrs p, const int L)
         lds_barrier();
     }
 
+    // the lane's offset into the state, recomputed here so that the compiler
+    // does not keep 64 addresses alive across the sweep
+    int so = 4 * g4 * PD + ncol + l16;
+    asm volatile("" : "+v"(so));
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                store_state_elem(st + (size_t)(16 * mt + 4 * g4 + r) * PD + ncol + 16 * nt + l16, S[mt][nt][r]);
+                store_state_elem(st + so + (16 * mt + r) * PD + 16 * nt, S[mt][nt][r]);
     // conv state after the sequence: the raw inputs of positions L-3, L-2,
     // L-1, where a position < 0 is a cached tap (read before this lane
     // overwrites it: conv_out may be conv_in, and each lane owns its channels)
