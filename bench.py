@@ -429,6 +429,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the chunked-prefill lines and print them as one JSON line "
+                         "(for profiling the prefill kernel alone)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then "
                          "WRITE_SIZE) into HBM bytes per decode launch, calibrated on the "
@@ -450,6 +453,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.only_prefill:
+        lines = [measure_prefill(M, L, sdt, max(5, args.steps // 20), 2) for M, L, sdt in PREFILL_SHAPES]
+        print(json.dumps({"prefill": lines}), flush=True)
+        return
 
     wl = kda_synth.WORKLOADS["glm_m32"]
     log(f"headline: {wl.description}")
