@@ -157,7 +157,8 @@ class Model:
 
 
 def time_model(model, steps, warmup, use_graph):
-    """Return (seconds for `steps` steps, mode)."""
+    """Return (seconds for `steps` steps, mode, per-step seconds).  An event
+    is recorded after every step as well, for the median and best step."""
     import torch
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -177,6 +178,7 @@ def time_model(model, steps, warmup, use_graph):
                 g.replay()
             stream.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         torch.cuda.synchronize()
         start.record(stream)
         for k in range(steps):
@@ -184,21 +186,65 @@ def time_model(model, steps, warmup, use_graph):
                 graphs[k % len(graphs)].replay()
             else:
                 model.step(k, sp)
+            marks[k].record(stream)
         end.record(stream)
         end.synchronize()
         torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3, ("hipGraph" if use_graph else "eager")
+    per_step = [(marks[k - 1] if k else start).elapsed_time(marks[k]) / 1e3 for k in range(steps)]
+    return start.elapsed_time(end) / 1e3, ("hipGraph" if use_graph else "eager"), per_step
 
 
-def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain", T=1):
+def replay_check(model, steps):
+    """The timed pass against an untimed one: from the same saved states, run
+    `steps` steps eagerly and again as hipGraph replays; True if the final
+    states and conv states agree bit for bit."""
+    import torch
+    saved = [(L["state"].clone(), L["conv"].clone()) for L in model.layers]
+
+    def restore():
+        for L, (st, cv) in zip(model.layers, saved):
+            L["state"].copy_(st)
+            L["conv"].copy_(cv)
+        torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    restore()
+    with torch.cuda.stream(stream):
+        for k in range(steps):
+            model.step(k, stream.cuda_stream)
+    stream.synchronize()
+    eager = [(L["state"].clone(), L["conv"].clone()) for L in model.layers]
+    restore()
+    with torch.cuda.stream(stream):
+        graphs = []
+        for t in range(model.n_inputs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                model.step(t, torch.cuda.current_stream().cuda_stream)
+            graphs.append(g)
+    restore()       # capture does not run the kernels, but start clean anyway
+    with torch.cuda.stream(stream):
+        for k in range(steps):
+            graphs[k % len(graphs)].replay()
+    stream.synchronize()
+    ok = all(torch.equal(L["state"], e[0]) and torch.equal(L["conv"], e[1]) for L, e in zip(model.layers, eager))
+    del saved, eager, graphs
+    torch.cuda.empty_cache()
+    return ok
+
+
+def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain", T=1, check=False):
     model = Model(wl, state_dtype, n_inputs, mode=mode, T=T)
     res = {}
     for use_graph in (False, True):
-        sec, mode = time_model(model, steps, warmup, use_graph)
+        sec, mode, per_step = time_model(model, steps, warmup, use_graph)
         launches = steps * wl.layers
+        srt = sorted(per_step)
         res[mode] = {
             "ms_per_step": sec * 1e3 / steps,
             "ms_per_layer": sec * 1e3 / launches,
+            "ms_per_layer_median_step": srt[len(srt) // 2] * 1e3 / wl.layers,
+            "ms_per_layer_best_step": srt[0] * 1e3 / wl.layers,
             "state_GBps": 2 * model.state_bytes_per_layer() * launches / sec / 1e9,
             "alg_GBps": model.alg_bytes_per_launch() * launches / sec / 1e9,
         }
@@ -208,6 +254,8 @@ def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain", T=1):
     out["modes"] = res
     out["alg_bytes_per_launch"] = model.alg_bytes_per_launch()
     out["state_bytes_per_launch"] = 2 * model.state_bytes_per_layer()
+    if check:
+        out["replay_bitwise_equal"] = replay_check(model, wl.steps)
     del model
     import torch
     torch.cuda.empty_cache()
@@ -336,10 +384,20 @@ def cpu_baseline(wl, budget_s=12.0):
             launches += 1
         layers += 1
     state_bytes = 2 * wl.state_bytes("f32") * launches
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": state_bytes / elapsed / 1e9,
         "unit": "GB/s",
         "cores": orc.max_threads(),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"{layers} of {wl.layers} layers x {wl.steps} steps of the same workload "
                   f"(M={wl.M}, 64x128x128; GB/s counts the FP32 state bytes the GPU moves), "
@@ -461,7 +519,7 @@ def main():
 
     wl = kda_synth.WORKLOADS["glm_m32"]
     log(f"headline: {wl.description}")
-    head = measure(wl, "f32", args.steps, args.warmup, n_inputs=wl.steps)
+    head = measure(wl, "f32", args.steps, args.warmup, n_inputs=wl.steps, check=True)
     log(f"  {json.dumps({k: head[k] for k in ('launch', 'ms_per_step', 'ms_per_layer', 'state_GBps')})}")
 
     secondary = []
@@ -539,6 +597,7 @@ def main():
         "ms_per_layer": head["ms_per_layer"],
         "frac_hbm_peak_state": head["state_GBps"] / HBM_PEAK_GBS,
         "modes": head["modes"],
+        "replay_bitwise_equal": head["replay_bitwise_equal"],
         "stream_ceiling": None if ceiling is None else {
             "rmw_GBps": ceiling["rmw"], "copy_GBps": ceiling["copy"],
             "kernel": "kda_probe_rmw / kda_probe_copy: 512 threads, one 16-byte non-temporal "
