@@ -156,9 +156,11 @@ class Model:
                 raise RuntimeError(f"{self.mode} decode step returned {rc}")
 
 
-def time_model(model, steps, warmup, use_graph):
-    """Return (seconds for `steps` steps, mode, per-step seconds).  An event
-    is recorded after every step as well, for the median and best step."""
+def time_model(model, steps, warmup, use_graph, per_step_events=False):
+    """Return (seconds for `steps` steps, mode, per-step seconds or None).
+    With per_step_events an event is recorded after every step (for the
+    median and best step); that marker costs time, so the pass that gives
+    the mean runs without it."""
     import torch
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -178,7 +180,7 @@ def time_model(model, steps, warmup, use_graph):
                 g.replay()
             stream.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)] if per_step_events else None
         torch.cuda.synchronize()
         start.record(stream)
         for k in range(steps):
@@ -186,11 +188,14 @@ def time_model(model, steps, warmup, use_graph):
                 graphs[k % len(graphs)].replay()
             else:
                 model.step(k, sp)
-            marks[k].record(stream)
+            if marks is not None:
+                marks[k].record(stream)
         end.record(stream)
         end.synchronize()
         torch.cuda.synchronize()
-    per_step = [(marks[k - 1] if k else start).elapsed_time(marks[k]) / 1e3 for k in range(steps)]
+    per_step = None
+    if marks is not None:
+        per_step = [(marks[k - 1] if k else start).elapsed_time(marks[k]) / 1e3 for k in range(steps)]
     return start.elapsed_time(end) / 1e3, ("hipGraph" if use_graph else "eager"), per_step
 
 
@@ -237,7 +242,8 @@ def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain", T=1, check=F
     model = Model(wl, state_dtype, n_inputs, mode=mode, T=T)
     res = {}
     for use_graph in (False, True):
-        sec, mode, per_step = time_model(model, steps, warmup, use_graph)
+        sec, mode, _ = time_model(model, steps, warmup, use_graph)
+        _, _, per_step = time_model(model, max(10, steps // 4), 1, use_graph, per_step_events=True)
         launches = steps * wl.layers
         srt = sorted(per_step)
         res[mode] = {

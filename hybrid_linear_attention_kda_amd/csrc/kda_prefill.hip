@@ -68,13 +68,25 @@ constexpr int PNT = 256;           // threads per workgroup (4 waves)
 constexpr int LS = PD + 4;         // LDS row stride of the [token][channel] arrays, floats
 constexpr int LT = PC + 4;         // LDS row stride of the 16 x 16 arrays, floats
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Three-way bf16 splits: x = x1 + x2 + x3 up to f32 rounding, each piece the
+// round-to-nearest-even bf16 of what the previous ones leave (the remainder
+// is exact in f32).  A product of two split operands then takes the six
+// terms x_a y_b with a + b <= 4 (pieces numbered from 1), which keeps
+// products to f32 accuracy while running on the bf16 matrix cores.
+// Fragments hold 8 bf16 (one per k slot of v_mfma_f32_16x16x32_bf16), as
+// 4 dwords, slot 2i in the low half of dword i.
 struct PrefillSmem {
-    float qh[PC][LS];              // q^ (normalised, scaled)
     float kh[PC][LS];              // k^; after the solve, -W
     float vv[PC][LS];              // v; after the solve, U
     float eg[PC][LS];              // Gamma (decay from the chunk start); after the state products, Delta
-    float ig[PC][LS];              // 1 / Gamma
-    float kt[PC][LS];              // (gamma_C / Gamma) . k^
+    union {
+        float qi[2][PC][LS];       // [0] q^ (normalised, scaled), [1] 1 / Gamma; dead after phase 2
+        u32x4 dp[3][4][2][2][16];  // Delta pieces [piece][wave][tile][token half][column]: 8 tokens each
+    };
+    u32x4 gqp[3][4][64];           // (Gamma . q^) pieces [piece][32-row block][lane]: A operand of the state products
+    u32x4 ktp[3][8][2][16];        // ((gamma_C / Gamma) . k^) pieces [piece][row tile][token half][row]
     float Z[PC][LT];               // Z[j][i] = sum_c (Gamma . k^)[i][c] (k^ / Gamma)[j][c]
     float P[PC][LT];               // Tril((Gamma . q^)(k^ / Gamma)^T), row = query token
     float gam[PD];                 // gamma_C, the decay over the whole chunk
@@ -87,42 +99,109 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+
+// two f32 -> packed bf16 (v_cvt_pk_bf16_f32, round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
+}
+
+// the three bf16 pieces of (a, b), one packed dword each
+__device__ __forceinline__ void split2(float a, float b, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+    p0 = cvt_pk_bf16(a, b);
+    const float a1 = a - bf16_lo(p0), b1 = b - bf16_hi(p0);
+    p1 = cvt_pk_bf16(a1, b1);
+    p2 = cvt_pk_bf16(a1 - bf16_lo(p1), b1 - bf16_hi(p1));
+}
+
+// the pieces of 8 values (slots 0..3 in lo, 4..7 in hi) as three fragments
+__device__ __forceinline__ void split8(f32x4 lo, f32x4 hi, u32x4 (&pc)[3]) {
+    uint32_t a[3], b[3], c[3], d[3];
+    split2(lo.x, lo.y, a[0], a[1], a[2]);
+    split2(lo.z, lo.w, b[0], b[1], b[2]);
+    split2(hi.x, hi.y, c[0], c[1], c[2]);
+    split2(hi.z, hi.w, d[0], d[1], d[2]);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) pc[q] = u32x4{a[q], b[q], c[q], d[q]};
+}
+
+// The six piece pairs (a, b) of a split product, 0-based: (0,0) (0,1) (1,0)
+// (0,2) (1,1) (2,0).  In the state update they are laid along k, two per
+// 32-slot MFMA: MFMA m takes pair 2m in slots 0..15 and pair 2m+1 in 16..31.
+__device__ constexpr int PAIR_A[6] = {0, 0, 1, 0, 1, 2};
+__device__ constexpr int PAIR_B[6] = {0, 1, 0, 2, 1, 0};
+
 __device__ __forceinline__ float load_state_elem(const float* s) { return *s; }
 __device__ __forceinline__ float load_state_elem(const uint16_t* s) { return bf16_lo(*s); }
 __device__ __forceinline__ void store_state_elem(float* s, float v) { *s = v; }
 __device__ __forceinline__ void store_state_elem(uint16_t* s, float v) { *s = (uint16_t)f32_to_bf16_rne(v); }
 
-// Sums over the 64 lanes of a wave for 16 values at once: returns, in every
-// lane, the total of v[lane >> 2].  Each exchange halves the values a lane
-// carries (lane bit 5 picks tokens 8..15, bit 4 the upper four of those, ...),
-// 17 exchanges instead of 16 x 6.
+// Cross-lane moves inside 16-lane rows (DPP, no LDS round trip): rotate by 8
+// (lane i <-> i ^ 8), mirror inside each 8-lane half, swaps inside quads.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_ROW_ROR8 = 0x128, DPP_HALF_MIRROR = 0x141, DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E;
+
+// Sums over the 64 lanes of a wave for 16 values at once.  Each exchange
+// halves the values a lane carries: lane bit 3 picks tokens 8..15 (partner
+// across the row rotation by 8), bit 2 the upper four of those (partner in
+// the mirrored half-row), bit 5 and bit 4 (partners 32 and 16 lanes away,
+// the only exchanges that leave the row); the last four lanes of a quad then
+// add up.  Lane l ends with the total of token 8 b3 + 4 b2 + 2 b5 + b4 of l;
+// sum16_lane(j) is a lane that holds token j's total.
 __device__ __forceinline__ float wave_sum16(const float (&v)[PC], int lane) {
     float a8[8], a4[4], a2[2];
-    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+    const bool b3 = lane & 8, b2 = lane & 4, b5 = lane & 32, b4 = lane & 16;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const float keep = b5 ? v[k + 8] : v[k], send = b5 ? v[k] : v[k + 8];
-        a8[k] = keep + __shfl_xor(send, 32, 64);
+        const float keep = b3 ? v[k + 8] : v[k], send = b3 ? v[k] : v[k + 8];
+        a8[k] = keep + dpp_mov<DPP_ROW_ROR8>(send);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const float keep = b4 ? a8[k + 4] : a8[k], send = b4 ? a8[k] : a8[k + 4];
-        a4[k] = keep + __shfl_xor(send, 16, 64);
+        const float keep = b2 ? a8[k + 4] : a8[k], send = b2 ? a8[k] : a8[k + 4];
+        a4[k] = keep + dpp_mov<DPP_HALF_MIRROR>(send);
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const float keep = b3 ? a4[k + 2] : a4[k], send = b3 ? a4[k] : a4[k + 2];
-        a2[k] = keep + __shfl_xor(send, 8, 64);
+        const float keep = b5 ? a4[k + 2] : a4[k], send = b5 ? a4[k] : a4[k + 2];
+        a2[k] = keep + __shfl_xor(send, 32, 64);
     }
-    const bool b2 = lane & 4;
-    float t = (b2 ? a2[1] : a2[0]) + __shfl_xor(b2 ? a2[0] : a2[1], 4, 64);
-    t += __shfl_xor(t, 2, 64);
-    t += __shfl_xor(t, 1, 64);
+    float t = (b4 ? a2[1] : a2[0]) + __shfl_xor(b4 ? a2[0] : a2[1], 16, 64);
+    t += dpp_mov<DPP_QUAD_XOR1>(t);
+    t += dpp_mov<DPP_QUAD_XOR2>(t);
     return t;
 }
 
+constexpr int sum16_lane(int j) { return 8 * (j >> 3) + 4 * ((j >> 2) & 1) + 32 * ((j >> 1) & 1) + 16 * (j & 1); }
+
 __device__ __forceinline__ float lane_value(float v, int src) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+// One column of (I + A) X = Diag(beta) R, right-looking, in place in cv:
+// c_i holds R_i minus the columns already solved, x_j = beta_j c_j once every
+// earlier column is in.  Z[j][i] = A'[i][j] (A = StrictTril(Diag(beta) A')).
+// The 256 entries of Z sit in the wave's registers (lane j + 16 (i / 4),
+// element i % 4) and beta in lanes 0..15; each coefficient comes to the
+// whole wave with one v_readlane, so the 16-step chain never waits on LDS.
+__device__ __forceinline__ void solve_column(float (&cv)[PC], const float (*Z)[LT], const float* beta, int lane) {
+    const f32x4 zv = lds4(&Z[lane & 15][4 * (lane >> 4)]);
+    const float bv = beta[lane & 15];
+#pragma unroll
+    for (int j = 0; j < PC; ++j) {
+        const float xj = lane_value(bv, j) * cv[j];
+        cv[j] = xj;
+#pragma unroll
+        for (int i = j + 1; i < PC; ++i) cv[i] = fmaf(-lane_value(zv[i & 3], j + 16 * (i >> 2)), xj, cv[i]);
+    }
 }
 
 }  // namespace
@@ -227,7 +306,7 @@ void prefill_kernel(const Ptrs p, const int L)
                 b0 = b1; b1 = b2; b2 = x1;
             }
             if (t0 + PC < L) fetch(t0 + PC);
-            float (*dst)[LS] = wv == 0 ? sm.qh : wv == 1 ? sm.kh : sm.vv;
+            float (*dst)[LS] = wv == 0 ? sm.qi[0] : wv == 1 ? sm.kh : sm.vv;
             if (wv < 2) {
                 float ss[PC];
 #pragma unroll
@@ -236,7 +315,7 @@ void prefill_kernel(const Ptrs p, const int L)
                 const float rn = (wv == 0 ? p.scale : 1.0f) * rsqrtf(tot + 1e-6f);
 #pragma unroll
                 for (int j = 0; j < PC; ++j) {
-                    const float rj = lane_value(rn, 4 * j);
+                    const float rj = lane_value(rn, sum16_lane(j));
                     z0[j] *= rj;
                     z1[j] *= rj;
                 }
@@ -256,7 +335,7 @@ void prefill_kernel(const Ptrs p, const int L)
                 e0 *= j < n ? exp_fast(g0) : 1.f;
                 e1 *= j < n ? exp_fast(g1) : 1.f;
                 *reinterpret_cast<float2*>(&sm.eg[j][2 * lane]) = make_float2(e0, e1);
-                *reinterpret_cast<float2*>(&sm.ig[j][2 * lane]) =
+                *reinterpret_cast<float2*>(&sm.qi[1][j][2 * lane]) =
                     make_float2(__builtin_amdgcn_rcpf(e0), __builtin_amdgcn_rcpf(e1));
             }
             *reinterpret_cast<float2*>(&sm.gam[2 * lane]) = make_float2(e0, e1);
@@ -273,7 +352,7 @@ void prefill_kernel(const Ptrs p, const int L)
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int c = 32 * g4 + 4 * q;
-                const f32x4 k4 = lds4(&sm.kh[l16][c]), e4 = lds4(&sm.eg[l16][c]), i4 = lds4(&sm.ig[l16][c]);
+                const f32x4 k4 = lds4(&sm.kh[l16][c]), e4 = lds4(&sm.eg[l16][c]), i4 = lds4(&sm.qi[1][l16][c]);
                 if (wv == 0) {
                     // D[i][j] = sum_c (Gamma k^)[i][c] (k^ / Gamma)[j][c] = Z[j][i]
                     acc0 = mfma16(k4.x * e4.x, k4.x * i4.x, acc0);
@@ -282,7 +361,7 @@ void prefill_kernel(const Ptrs p, const int L)
                     acc1 = mfma16(k4.w * e4.w, k4.w * i4.w, acc1);
                 } else {
                     // D[s][t] = sum_c (k^ / Gamma)[s][c] (Gamma q^)[t][c] = P[t][s]
-                    const f32x4 q4 = lds4(&sm.qh[l16][c]);
+                    const f32x4 q4 = lds4(&sm.qi[0][l16][c]);
                     acc0 = mfma16(k4.x * i4.x, q4.x * e4.x, acc0);
                     acc1 = mfma16(k4.y * i4.y, q4.y * e4.y, acc1);
                     acc0 = mfma16(k4.z * i4.z, q4.z * e4.z, acc0);
@@ -299,79 +378,104 @@ void prefill_kernel(const Ptrs p, const int L)
                 *reinterpret_cast<f32x4*>(&sm.Z[l16][4 * g4]) = d;
             }
         } else {
-            for (int e = tid - 128; e < PC * (PD / 4); e += 128) {
-                const int j = e >> 5, c = 4 * (e & 31);
-                const f32x4 k4 = lds4(&sm.kh[j][c]), i4 = lds4(&sm.ig[j][c]), gm = lds4(&sm.gam[c]);
-                *reinterpret_cast<f32x4*>(&sm.kt[j][c]) = k4 * (gm * i4);
+            // bf16 pieces of the two A operands of phases 4 and 5, in
+            // fragment order so that those reads are contiguous
+            const int tt = tid - 128;
+#pragma unroll
+            for (int f = tt; f < 256; f += 128) {
+                // Gamma . q^: fragment (32-row block kb, lane ln) holds token
+                // ln % 16 at the 8 state rows the state's own lanes carry
+                const int kb = f >> 6, ln = f & 63, tk = ln & 15, c0 = 32 * kb + 4 * (ln >> 4);
+                u32x4 pc[3];
+                split8(lds4(&sm.qi[0][tk][c0]) * lds4(&sm.eg[tk][c0]),
+                       lds4(&sm.qi[0][tk][c0 + 16]) * lds4(&sm.eg[tk][c0 + 16]), pc);
+#pragma unroll
+                for (int q = 0; q < 3; ++q) sm.gqp[q][kb][ln] = pc[q];
+            }
+#pragma unroll
+            for (int f = tt; f < 256; f += 128) {
+                // (gamma_C / Gamma) . k^: fragment (row tile mt, token half hf,
+                // row) holds 8 tokens of state row 16 mt + row
+                const int mt = f >> 5, hf = (f >> 4) & 1, k = 16 * mt + (f & 15);
+                const float gk = sm.gam[k];
+                float v[8];
+#pragma unroll
+                for (int s2 = 0; s2 < 8; ++s2) v[s2] = sm.kh[8 * hf + s2][k] * (gk * sm.qi[1][8 * hf + s2][k]);
+                u32x4 pc[3];
+                split8(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}, pc);
+#pragma unroll
+                for (int q = 0; q < 3; ++q) sm.ktp[q][mt][hf][f & 15] = pc[q];
             }
         }
         lds_barrier();
 
-        // ---- 3. (I + A) W = Diag(beta)(Gamma . K), (I + A) U = Diag(beta) V; (Gamma . Q) S ----
-        // Right-looking: c_i holds the right-hand side minus the columns
-        // already solved; x_j = beta_j c_j once every earlier column is in.
-        // Waves 0, 1 solve for W (stored negated), waves 2, 3 for U.  The
-        // matrix cores meanwhile form (Gamma . Q) S for this wave's columns,
-        // Gamma . q^ made on the fly; the two are independent, so one block
-        // lets the scheduler interleave them.
-        f32x4 oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // ---- 3. (I + A) W = Diag(beta)(Gamma . K), (I + A) U = Diag(beta) V ----
+        // Waves 0, 1 solve for W (stored negated), waves 2, 3 for U.
         {
-            const bool isw = wv < 2;
             const int col = tid & (PD - 1);
-            float (*X)[LS] = isw ? sm.kh : sm.vv;
+            float (*X)[LS] = wv < 2 ? sm.kh : sm.vv;
             float cv[PC];
+            if (wv < 2) {
 #pragma unroll
-            for (int j = 0; j < PC; ++j) cv[j] = X[j][col] * (isw ? sm.eg[j][col] : 1.0f);
-            const f32x4 bb0 = lds4(&sm.beta[0]), bb1 = lds4(&sm.beta[4]), bb2 = lds4(&sm.beta[8]), bb3 = lds4(&sm.beta[12]);
-            const float bt[PC] = {bb0.x, bb0.y, bb0.z, bb0.w, bb1.x, bb1.y, bb1.z, bb1.w,
-                                  bb2.x, bb2.y, bb2.z, bb2.w, bb3.x, bb3.y, bb3.z, bb3.w};
+                for (int j = 0; j < PC; ++j) cv[j] = sm.kh[j][col] * sm.eg[j][col];
+            } else {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const f32x4 q4 = lds4(&sm.qh[l16][16 * mt + 4 * g4]), e4 = lds4(&sm.eg[l16][16 * mt + 4 * g4]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float a = q4[r] * e4[r];
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) oacc[nt] = mfma16(a, S[mt][nt][r], oacc[nt]);
-                }
+                for (int j = 0; j < PC; ++j) cv[j] = sm.vv[j][col];
             }
-#pragma unroll
-            for (int j = 0; j < PC; ++j) {
-                const float xj = bt[j] * cv[j];
-                cv[j] = xj;
-#pragma unroll
-                for (int q = (j + 1) / 4; q < PC / 4; ++q) {
-                    const f32x4 z = lds4(&sm.Z[j][4 * q]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (4 * q + r > j) cv[4 * q + r] = fmaf(-z[r], xj, cv[4 * q + r]);
-                }
-            }
+            solve_column(cv, sm.Z, sm.beta, lane);
             // each thread reads and overwrites only its own column of k^ or v
+            const float sg = wv < 2 ? -1.0f : 1.0f;
 #pragma unroll
-            for (int j = 0; j < PC; ++j) X[j][col] = isw ? -cv[j] : cv[j];
+            for (int j = 0; j < PC; ++j) X[j][col] = cv[j] * sg;
         }
         lds_barrier();
 
-        // ---- 4. Delta = U - W S, this wave's 32 value columns ----
-        f32x4 dacc[2];
+        // ---- 4. Delta = U - W S and (Gamma . Q) S, this wave's 32 value columns ----
+        // Per 32-row block of the state: the lane's 8 state values of each
+        // column tile (rows 32 kb + 4 (lane / 16) + {0..3, 16..19}: its own
+        // registers) are the B fragment; the A fragments (-W and Gamma . q^
+        // of token lane % 16 at the same rows) come split from LDS.  Six bf16
+        // products per pair of split operands.
+        f32x4 dacc[2], oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) dacc[nt][r] = sm.vv[4 * g4 + r][ncol + 16 * nt + l16];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const f32x4 w4 = lds4(&sm.kh[l16][16 * mt + 4 * g4]);   // -W
+        for (int kb = 0; kb < 4; ++kb) {
+            u32x4 sb[2][3], wp[3], gp[3];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int nt = 0; nt < 2; ++nt)
+                split8(f32x4{S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3]},
+                       f32x4{S[2 * kb + 1][nt][0], S[2 * kb + 1][nt][1], S[2 * kb + 1][nt][2], S[2 * kb + 1][nt][3]},
+                       sb[nt]);
+            split8(lds4(&sm.kh[l16][32 * kb + 4 * g4]), lds4(&sm.kh[l16][32 * kb + 16 + 4 * g4]), wp);   // -W
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) dacc[nt] = mfma16(w4[r], S[mt][nt][r], dacc[nt]);
+            for (int q = 0; q < 3; ++q) gp[q] = sm.gqp[q][kb][lane];
+#pragma unroll
+            for (int pr = 0; pr < 6; ++pr)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    dacc[nt] = mfma_bf16(wp[PAIR_A[pr]], sb[nt][PAIR_B[pr]], dacc[nt]);
+                    oacc[nt] = mfma_bf16(gp[PAIR_A[pr]], sb[nt][PAIR_B[pr]], oacc[nt]);
+                }
         }
-        // Delta replaces Gamma, which nobody reads any more
+        // Delta replaces Gamma, which nobody reads any more; its pieces go
+        // where q^ and 1 / Gamma were: this lane's 4 tokens 4 (lane / 16) + r
+        // are half of the fragment of token half (lane / 32)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.eg[4 * g4 + r][ncol + 16 * nt + l16] = dacc[nt][r];
+            uint32_t p0a, p1a, p2a, p0b, p1b, p2b;
+            split2(dacc[nt][0], dacc[nt][1], p0a, p1a, p2a);
+            split2(dacc[nt][2], dacc[nt][3], p0b, p1b, p2b);
+            u32x2* const dst = reinterpret_cast<u32x2*>(&sm.dp[0][wv][nt][g4 >> 1][l16]) + (g4 & 1);
+            constexpr int PIECE = sizeof(sm.dp[0]) / sizeof(u32x2);
+            dst[0] = u32x2{p0a, p0b};
+            dst[PIECE] = u32x2{p1a, p1b};
+            dst[2 * PIECE] = u32x2{p2a, p2b};
+        }
         lds_barrier();
 
         // ---- 5. O = (Gamma . Q) S + P Delta; S' = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta ----
@@ -396,19 +500,31 @@ void prefill_kernel(const Ptrs p, const int L)
                 }
             }
         }
+        // state update: the contraction runs over the 16 tokens of each of
+        // the six piece pairs, 96 k slots = three MFMAs; lane / 16 = 2 s + hh
+        // takes pair 2 m + s, tokens 8 hh .. 8 hh + 7
+        {
+            const int hh = g4 & 1, sel = g4 >> 1;
+            u32x4 db[3][2];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const f32x4 gm = lds4(&sm.gam[16 * mt + 4 * g4]);
-            float a[4];
+            for (int mm = 0; mm < 3; ++mm)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) a[kk] = sm.kt[4 * g4 + kk][16 * mt + l16];
+                for (int nt = 0; nt < 2; ++nt)
+                    db[mm][nt] = sm.dp[sel ? PAIR_B[2 * mm + 1] : PAIR_B[2 * mm]][wv][nt][hh][l16];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x4 acc = {S[mt][nt][0] * gm.x, S[mt][nt][1] * gm.y, S[mt][nt][2] * gm.z, S[mt][nt][3] * gm.w};
+            for (int mt = 0; mt < 8; ++mt) {
+                const f32x4 gm = lds4(&sm.gam[16 * mt + 4 * g4]);
+                u32x4 ka[3];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acc = mfma16(a[kk], dl[nt][kk], acc);
+                for (int mm = 0; mm < 3; ++mm) ka[mm] = sm.ktp[sel ? PAIR_A[2 * mm + 1] : PAIR_A[2 * mm]][mt][hh][l16];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[mt][nt][r] = acc[r];
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x4 acc = {S[mt][nt][0] * gm.x, S[mt][nt][1] * gm.y, S[mt][nt][2] * gm.z, S[mt][nt][3] * gm.w};
+#pragma unroll
+                    for (int mm = 0; mm < 3; ++mm) acc = mfma_bf16(ka[mm], db[mm][nt], acc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[mt][nt][r] = acc[r];
+                }
             }
         }
         // the next chunk's inputs overwrite every array above
