@@ -20,14 +20,11 @@
 // matrix products).
 //
 // Design (MI355X, CDNA4): one workgroup of 4 waves per (stream, head) sweeps
-// the head's chunks in order.  The head's 128 x 128 f32 state stays in the
-// accumulator registers of v_mfma_f32_16x16x4f32 for the whole sequence:
-// wave w owns value columns [32w, 32w + 32), each lane 64 state values in the
-// instruction's output layout (row k = 16 mt + 4 (lane / 16) + r, column
-// n = 32 w + 16 nt + lane % 16).  That layout is also a valid B operand for
-// W S and (Gamma . Q) S when the contraction index is enumerated in the same
-// order, so the state is never rearranged.  Per chunk, five phases separated
-// by workgroup barriers:
+// the head's chunks in order, two workgroups per CU.  The head's 128 x 128
+// f32 state stays in the accumulator layout of the 16 x 16 MFMAs for the
+// whole sequence: wave w owns value columns [32w, 32w + 32), each lane 64
+// state values (row k = 16 mt + 4 (lane / 16) + r, column n = 32 w + 16 nt +
+// lane % 16).  Per chunk, five phases:
 //
 //   1. inputs: waves 0, 1, 2 run the conv + SiLU of q, k, v (each lane two
 //      channels over the chunk's 16 tokens, the three previous raw inputs
@@ -36,20 +33,29 @@
 //      the forget gate, its running decay product and the write strengths.
 //      The raw inputs of the next chunk are then requested, so their HBM
 //      latency hides behind phases 2 to 5.
-//   2. A (wave 0) and P (wave 1) as 16 x 16 products over the 128 channels;
-//      waves 2 and 3 form (gamma_C / Gamma) . K.
+//   2. A (wave 0) and P (wave 1) as 16 x 16 products over the 128 channels
+//      (f32 MFMA); waves 2 and 3 split Gamma . Q and (gamma_C / Gamma) . K
+//      into bf16 pieces, in MFMA fragment order.
 //   3. the triangular solves for W and U, right-looking, one column per
-//      thread (256 columns), straight from (I + A) W = Diag(beta)(Gamma . K),
-//      while the matrix cores form (Gamma . Q) S (64 MFMA per wave).
-//   4. Delta = U - W S on all four waves (64 MFMA each).
-//   5. O = (Gamma . Q) S + P Delta, stored; S' (64 MFMA each).
+//      thread (256 columns), straight from (I + A) W = Diag(beta)(Gamma . K).
+//   4. Delta = U - W S and (Gamma . Q) S; each wave needs only its own
+//      columns of Delta afterwards, so no workgroup barrier separates it
+//      from phase 5.
+//   5. O = (Gamma . Q) S + P Delta, stored; S' = Diag(gamma_C) S + ...
 //
-// LDS rows of the [token][channel] arrays are padded to 132 floats: operand
-// reads with the row chosen by lane % 16 and four consecutive channels per
-// lane (ds_read_b128) and reads with the token chosen by lane / 16 both land
-// on distinct banks.  Where the contraction runs over tokens, the MFMA's k
-// slot lane / 16 stands for tokens 4 (lane / 16) + kk, which keeps those
-// reads conflict-free as well.
+// The three state products (phases 4 and 5) run on the bf16 matrix cores
+// from three-way bf16 splits of both operands, six piece pairs per product,
+// f32 accumulation: FP32 accuracy at a fraction of the f32 MFMA time (f32
+// MFMA shares its issue budget with vector work on this chip; bf16 MFMA is
+// 16 times faster per flop).  The state's own registers of a 32-row block
+// (rows 32 kb + 4 (lane / 16) + {0..3, 16..19}) form the B fragment of
+// v_mfma_f32_16x16x32_bf16 directly.
+//
+// LDS: the [token][channel] arrays have rows of 132 floats; the bf16
+// fragment arrays are lane-major, so a half-wave reads 512 contiguous bytes
+// (row-strided 16-byte reads cost several times a contiguous one).  Where a
+// 16 x 16 x 4 contraction runs over tokens, the MFMA's k slot lane / 16
+// stands for tokens 4 (lane / 16) + kk.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -98,6 +104,14 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 }
 
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// Orders this wave's LDS writes before its later LDS reads (data handed
+// between lanes of one wave), without waiting for the other waves.
+__device__ __forceinline__ void lds_wave_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
@@ -476,7 +490,8 @@ void prefill_kernel(const Ptrs p, const int L)
             dst[PIECE] = u32x2{p1a, p1b};
             dst[2 * PIECE] = u32x2{p2a, p2b};
         }
-        lds_barrier();
+        // phase 5 reads only this wave's columns of Delta and its own pieces
+        lds_wave_fence();
 
         // ---- 5. O = (Gamma . Q) S + P Delta; S' = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta ----
         // contraction over tokens: the k slot lane / 16 is token 4 (lane / 16) + kk
