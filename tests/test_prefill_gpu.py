@@ -115,3 +115,43 @@ def test_prefill_empty():
                       gp["A_log"], gp["dt_bias"], e(1, 0, 2), wl.scale, e(1, 0, 2, 128))
     torch.cuda.synchronize()
     assert torch.equal(S, li["state"])
+
+
+# The benchmark's prefill shapes, inputs and launch (bench.py's measure_prefill:
+# workload name prefill_m{M}_l{L}, seed 7, whole-sequence draws, lower bound -5),
+# checked on sampled (stream, head) units over every token of the sequence.
+BENCH_SHAPES = [(8, 2048, "f32"), (32, 1024, "bf16"), (1, 8192, "f32")]
+
+
+@pytest.mark.parametrize("M,L,state_dtype", BENCH_SHAPES)
+def test_prefill_benchmark_shapes_sampled(orc, M, L, state_dtype):
+    H, D = 64, 128
+    wl = kda_synth.custom(f"prefill_m{M}_l{L}", M, H, D, steps=L, seed=7)
+    li = kda_synth.layer_inputs(wl, 0, DEV, state_dtype)
+    gp = kda_synth.gate_params(wl, 0, DEV)
+    seq = kda_synth.sequence_inputs(wl, 0, L, DEV)
+    S, cs = li["state"], li["conv_state"]
+    o = torch.empty((M, L, H, D), dtype=torch.bfloat16, device=DEV)
+    units = sorted({(0, 0), (M - 1, H - 1), (M // 2, 17), (min(1, M - 1), 40)})
+    S0 = {u: host(S[u[0], u[1]]) for u in units}
+    cs0 = host(cs)
+    kda_prefill_gated(S, seq["x"], li["conv_w"], cs, cs, seq["f"], gp["A_log"], gp["dt_bias"],
+                      seq["beta_logit"], wl.scale, o)
+    torch.cuda.synchronize()
+    cw = host(li["conv_w"]).reshape(3, H, D, 4)
+    tol_s = TOL_STATE_PREFILL if state_dtype == "f32" else 4e-3
+    worst_s = worst_o = 0.0
+    for (m, h) in units:
+        sl = slice(h * D, (h + 1) * D)
+        xu = host(seq["x"][m, :, :, sl]).reshape(1, L, 3, D)
+        S_ref, _, o_ref = orc.sequence_gated(
+            S0[(m, h)][None, None], xu, cw[:, h].reshape(3 * D, 4),
+            cs0[m].reshape(3, 3, H, D)[:, :, h].reshape(1, 3, 3 * D),
+            host(seq["f"][m, :, sl])[None], host(gp["A_log"][h:h + 1]), host(gp["dt_bias"][sl]),
+            host(seq["beta_logit"][m, :, h:h + 1])[None], wl.scale)
+        e_s = rel_err(host(S[m, h]), S_ref[0, 0])
+        e_o = rel_err(host(o[m, :, h]), o_ref[0, :, 0])
+        worst_s, worst_o = max(worst_s, e_s), max(worst_o, e_o)
+        assert e_s <= tol_s, f"state ({m},{h}): {e_s:.3e}"
+        assert e_o <= TOL_O, f"outputs ({m},{h}): {e_o:.3e}"
+    say(f"prefill {M} x {L} tokens {state_dtype}, units {units}: state {worst_s:.3e} o {worst_o:.3e}")
