@@ -63,8 +63,9 @@ PREFILL_CHUNK = 16
 PREFILL_TOKEN_BYTES, PREFILL_STREAM_BYTES = 82_048, 294_912
 PREFILL_LAYER_BYTES = 196_608 + 32_768 + 256
 MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X dense FP32 matrix
-# (streams, tokens per stream, state dtype) of the prefill lines
-PREFILL_SHAPES = ((8, 2048, "f32"), (1, 8192, "f32"), (32, 1024, "bf16"))
+# (streams, tokens per stream, state dtype) of the prefill lines; the last two are
+# the T-token shapes of kda_decode_multi, for the chunked path
+PREFILL_SHAPES = ((8, 2048, "f32"), (1, 8192, "f32"), (32, 1024, "bf16"), (32, 8, "f32"), (32, 16, "f32"))
 
 
 def log(msg):

@@ -120,7 +120,7 @@ def test_prefill_empty():
 # The benchmark's prefill shapes, inputs and launch (bench.py's measure_prefill:
 # workload name prefill_m{M}_l{L}, seed 7, whole-sequence draws, lower bound -5),
 # checked on sampled (stream, head) units over every token of the sequence.
-BENCH_SHAPES = [(8, 2048, "f32"), (32, 1024, "bf16"), (1, 8192, "f32")]
+BENCH_SHAPES = [(8, 2048, "f32"), (32, 1024, "bf16"), (1, 8192, "f32"), (32, 8, "f32"), (32, 16, "f32")]
 
 
 @pytest.mark.parametrize("M,L,state_dtype", BENCH_SHAPES)
