@@ -253,7 +253,7 @@ int kda_decode_step_split(int M, int H, int D, int state_dtype, void* state, con
 int kda_decode_multi(int T, int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
                      const void* conv_w, const void* conv_in, void* conv_out, const float* alpha,
                      const float* beta, float scale, void* o, void* stream) {
-    if (T < 0) return KDA_ERR_ARG;
+    if (T < 0 || T > KDA_MAX_TOKENS) return KDA_ERR_ARG;
     int rc = check_common(M, H, D, state_dtype, scale);
     if (rc != KDA_OK) return rc;
     if (M == 0 || T == 0) return KDA_OK;
@@ -293,7 +293,7 @@ int kda_prefill_gated(int L, int M, int H, int D, int state_dtype, void* state, 
                       const void* conv_w, const void* conv_in, void* conv_out, const void* f_gate,
                       const float* A_log, const float* dt_bias, const void* beta_logit,
                       float gate_lower_bound, float scale, void* o, void* stream) {
-    if (L < 0) return KDA_ERR_ARG;
+    if (L < 0 || L > KDA_MAX_TOKENS) return KDA_ERR_ARG;
     int rc = check_common(M, H, D, state_dtype, scale);
     if (rc != KDA_OK) return rc;
     if (D != 128) return KDA_ERR_SHAPE;

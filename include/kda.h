@@ -52,6 +52,11 @@ enum {
 };
 
 /* Storage type of the recurrent state.  Arithmetic is f32 either way. */
+/* Largest token count per stream of one kda_decode_multi or
+ * kda_prefill_gated call (2^30): keeps every token index of the kernels'
+ * chunk loops inside int. */
+#define KDA_MAX_TOKENS (1 << 30)
+
 typedef enum { KDA_STATE_F32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype;
 
 /* Forget-gate forms ("GLM-5.3 deep dive", 8.2.3, the gate as fla computes
@@ -181,7 +186,8 @@ int kda_decode_layer_step(int M, int H, int D, int state_dtype,
  * storage it is also rounded once per call).  For speculative/MTP
  * verification and short prefill.
  *
- *  T       tokens per stream, >= 0 (T == 0 or M == 0: nothing is touched).
+ *  T       tokens per stream, 0 <= T <= KDA_MAX_TOKENS (T == 0 or M == 0:
+ *          nothing is touched; above the cap: KDA_ERR_ARG).
  *  x_qkv   [M][T][3][H*D]  bf16 pre-conv q|k|v of each token.
  *  alpha   [M][T][H][D]    f32.
  *  beta    [M][T][H]       f32.
@@ -205,7 +211,8 @@ int kda_decode_multi(int T, int M, int H, int D, int state_dtype,
  * beta = sigmoid(logit), gated delta rule, readout), reordered into matrix
  * products over chunks of 16 tokens.
  *
- *  L          tokens per stream, >= 0 (L == 0 or M == 0: nothing is touched).
+ *  L          tokens per stream, 0 <= L <= KDA_MAX_TOKENS (L == 0 or M == 0:
+ *             nothing is touched; above the cap: KDA_ERR_ARG).
  *  D          must be 128.
  *  x_qkv      [M][L][3][H*D]  bf16 pre-conv q|k|v.
  *  f_gate     [M][L][H*D]     bf16 raw forget-gate projection.

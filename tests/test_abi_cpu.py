@@ -221,6 +221,7 @@ def test_multi_errors(lib):
         s, x, w, ci, co, a, b, o = ptrs
         return lib.kda_decode_multi(T, M, H, D, sdt, s, x, w, ci, co, a, b, scale, o, None)
     assert call(T=-1) == binding.KDA_ERR_ARG
+    assert call(T=(1 << 30) + 1) == binding.KDA_ERR_ARG     # above KDA_MAX_TOKENS
     assert call(M=-1) == binding.KDA_ERR_ARG
     assert call(D=100) == binding.KDA_ERR_SHAPE
     assert call(sdt=9) == binding.KDA_ERR_DTYPE
@@ -251,6 +252,7 @@ def test_prefill_errors(lib):
         s, x, w, ci, co, f, A, b, bl, o = ptrs
         return lib.kda_prefill_gated(L, M, H, D, sdt, s, x, w, ci, co, f, A, b, bl, lb, scale, o, None)
     assert call(L=-1) == binding.KDA_ERR_ARG
+    assert call(L=(1 << 30) + 1) == binding.KDA_ERR_ARG     # above KDA_MAX_TOKENS
     assert call(D=64) == binding.KDA_ERR_SHAPE
     assert call(sdt=4) == binding.KDA_ERR_DTYPE
     for lb in (-5.5, 0.0, 0.5, math.nan, -math.inf):
