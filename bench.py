@@ -308,8 +308,8 @@ def measure_prefill(M, L, state_dtype, steps, warmup, H=64, D=128):
         e.record(stream)
         e.synchronize()
     sec = s.elapsed_time(e) / 1e3 / steps
-    chunks = -(-L // PREFILL_CHUNK)
-    flops = PREFILL_FLOPS_PER_CHUNK_HEAD * chunks * M * H
+    # per token (a ragged last chunk counts its tokens, not the padded 16)
+    flops = PREFILL_FLOPS_PER_CHUNK_HEAD * M * H * L // PREFILL_CHUNK
     nbytes = (M * (L * PREFILL_TOKEN_BYTES + PREFILL_STREAM_BYTES) + PREFILL_LAYER_BYTES
               + 2 * wl.state_bytes(state_dtype))
     del li, gp, seq, o
