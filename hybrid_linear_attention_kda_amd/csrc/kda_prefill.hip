@@ -33,9 +33,10 @@
 //      the forget gate, its running decay product and the write strengths.
 //      The raw inputs of the next chunk are then requested, so their HBM
 //      latency hides behind phases 2 to 5.
-//   2. A (wave 0) and P (wave 1) as 16 x 16 products over the 128 channels
-//      (f32 MFMA); waves 2 and 3 split Gamma . Q and (gamma_C / Gamma) . K
-//      into bf16 pieces, in MFMA fragment order.
+//   2. A (waves 0, 1) and P (waves 2, 3) as 16 x 16 products, each wave
+//      over one half of the 128 channels (f32 MFMA; the halves are added
+//      where A and P are read); then all waves split Gamma . Q and
+//      (gamma_C / Gamma) . K into bf16 pieces, in MFMA fragment order.
 //   3. the triangular solves for W and U, right-looking, one column per
 //      thread (256 columns), straight from (I + A) W = Diag(beta)(Gamma . K).
 //   4. Delta = U - W S and (Gamma . Q) S; each wave needs only its own
@@ -93,8 +94,8 @@ struct PrefillSmem {
     };
     u32x4 gqp[3][4][64];           // (Gamma . q^) pieces [piece][32-row block][lane]: A operand of the state products
     u32x4 ktp[3][8][2][16];        // ((gamma_C / Gamma) . k^) pieces [piece][row tile][token half][row]
-    float Z[PC][LT];               // Z[j][i] = sum_c (Gamma . k^)[i][c] (k^ / Gamma)[j][c]
-    float P[PC][LT];               // Tril((Gamma . q^)(k^ / Gamma)^T), row = query token
+    float Z[2][PC][LT];            // Z[j][i] = sum_c (Gamma . k^)[i][c] (k^ / Gamma)[j][c], per channel half
+    float P[2][PC][LT];            // Tril((Gamma . q^)(k^ / Gamma)^T), row = query token, per channel half
     float gam[PD];                 // gamma_C, the decay over the whole chunk
     float beta[PC];
 };
@@ -202,12 +203,13 @@ __device__ __forceinline__ float lane_value(float v, int src) {
 
 // One column of (I + A) X = Diag(beta) R, right-looking, in place in cv:
 // c_i holds R_i minus the columns already solved, x_j = beta_j c_j once every
-// earlier column is in.  Z[j][i] = A'[i][j] (A = StrictTril(Diag(beta) A')).
+// earlier column is in.  Z[0] + Z[1] (the two channel halves) holds
+// A'[i][j] at [j][i] (A = StrictTril(Diag(beta) A')).
 // The 256 entries of Z sit in the wave's registers (lane j + 16 (i / 4),
 // element i % 4) and beta in lanes 0..15; each coefficient comes to the
 // whole wave with one v_readlane, so the 16-step chain never waits on LDS.
-__device__ __forceinline__ void solve_column(float (&cv)[PC], const float (*Z)[LT], const float* beta, int lane) {
-    const f32x4 zv = lds4(&Z[lane & 15][4 * (lane >> 4)]);
+__device__ __forceinline__ void solve_column(float (&cv)[PC], const float (*Z)[PC][LT], const float* beta, int lane) {
+    const f32x4 zv = lds4(&Z[0][lane & 15][4 * (lane >> 4)]) + lds4(&Z[1][lane & 15][4 * (lane >> 4)]);
     const float bv = beta[lane & 15];
 #pragma unroll
     for (int j = 0; j < PC; ++j) {
@@ -359,58 +361,56 @@ void prefill_kernel(const Ptrs p, const int L)
         }
         lds_barrier();
 
-        // ---- 2. A and P over the channels (waves 0, 1); (gamma_C / Gamma) . k^ (waves 2, 3) ----
-        if (wv < 2) {
-            // lane / 16 takes channels [32 (lane / 16), 32 (lane / 16) + 32)
+        // ---- 2. A (waves 0, 1) and P (waves 2, 3), each wave one half of the
+        // channels; then the bf16 pieces of the A operands of phases 4 and 5 ----
+        {
+            // lane / 16 takes channels [cb + 16 (lane / 16), cb + 16 (lane / 16) + 16)
+            const int cb = 64 * (wv & 1);
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            if (wv < 2) {
+                // D[i][j] = sum_c (Gamma k^)[i][c] (k^ / Gamma)[j][c] = Z[j][i]
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int c = 32 * g4 + 4 * q;
-                const f32x4 k4 = lds4(&sm.kh[l16][c]), e4 = lds4(&sm.eg[l16][c]), i4 = lds4(&sm.qi[1][l16][c]);
-                if (wv == 0) {
-                    // D[i][j] = sum_c (Gamma k^)[i][c] (k^ / Gamma)[j][c] = Z[j][i]
+                for (int q = 0; q < 4; ++q) {
+                    const int c = cb + 16 * g4 + 4 * q;
+                    const f32x4 k4 = lds4(&sm.kh[l16][c]), e4 = lds4(&sm.eg[l16][c]), i4 = lds4(&sm.qi[1][l16][c]);
                     acc0 = mfma16(k4.x * e4.x, k4.x * i4.x, acc0);
                     acc1 = mfma16(k4.y * e4.y, k4.y * i4.y, acc1);
                     acc0 = mfma16(k4.z * e4.z, k4.z * i4.z, acc0);
                     acc1 = mfma16(k4.w * e4.w, k4.w * i4.w, acc1);
-                } else {
-                    // D[s][t] = sum_c (k^ / Gamma)[s][c] (Gamma q^)[t][c] = P[t][s]
-                    const f32x4 q4 = lds4(&sm.qi[0][l16][c]);
+                }
+                *reinterpret_cast<f32x4*>(&sm.Z[wv & 1][l16][4 * g4]) = acc0 + acc1;
+            } else {
+                // D[s][t] = sum_c (k^ / Gamma)[s][c] (Gamma q^)[t][c] = P[t][s]
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = cb + 16 * g4 + 4 * q;
+                    const f32x4 k4 = lds4(&sm.kh[l16][c]), i4 = lds4(&sm.qi[1][l16][c]);
+                    const f32x4 q4 = lds4(&sm.qi[0][l16][c]), e4 = lds4(&sm.eg[l16][c]);
                     acc0 = mfma16(k4.x * i4.x, q4.x * e4.x, acc0);
                     acc1 = mfma16(k4.y * i4.y, q4.y * e4.y, acc1);
                     acc0 = mfma16(k4.z * i4.z, q4.z * e4.z, acc0);
                     acc1 = mfma16(k4.w * i4.w, q4.w * e4.w, acc1);
                 }
-            }
-            f32x4 d = acc0 + acc1;
-            if (wv == 1) {
+                f32x4 d = acc0 + acc1;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (4 * g4 + r > l16) d[r] = 0.f;     // keep s <= t
-                *reinterpret_cast<f32x4*>(&sm.P[l16][4 * g4]) = d;
-            } else {
-                *reinterpret_cast<f32x4*>(&sm.Z[l16][4 * g4]) = d;
+                *reinterpret_cast<f32x4*>(&sm.P[wv & 1][l16][4 * g4]) = d;
             }
-        } else {
-            // bf16 pieces of the two A operands of phases 4 and 5, in
-            // fragment order so that those reads are contiguous
-            const int tt = tid - 128;
-#pragma unroll
-            for (int f = tt; f < 256; f += 128) {
-                // Gamma . q^: fragment (32-row block kb, lane ln) holds token
-                // ln % 16 at the 8 state rows the state's own lanes carry
-                const int kb = f >> 6, ln = f & 63, tk = ln & 15, c0 = 32 * kb + 4 * (ln >> 4);
+            // Gamma . q^: fragment (32-row block kb, lane ln) holds token ln % 16
+            // at the 8 state rows the state's own lanes carry
+            {
+                const int kb = tid >> 6, ln = tid & 63, tk = ln & 15, c0 = 32 * kb + 4 * (ln >> 4);
                 u32x4 pc[3];
                 split8(lds4(&sm.qi[0][tk][c0]) * lds4(&sm.eg[tk][c0]),
                        lds4(&sm.qi[0][tk][c0 + 16]) * lds4(&sm.eg[tk][c0 + 16]), pc);
 #pragma unroll
                 for (int q = 0; q < 3; ++q) sm.gqp[q][kb][ln] = pc[q];
             }
-#pragma unroll
-            for (int f = tt; f < 256; f += 128) {
-                // (gamma_C / Gamma) . k^: fragment (row tile mt, token half hf,
-                // row) holds 8 tokens of state row 16 mt + row
-                const int mt = f >> 5, hf = (f >> 4) & 1, k = 16 * mt + (f & 15);
+            // (gamma_C / Gamma) . k^: fragment (row tile mt, token half hf, row)
+            // holds 8 tokens of state row 16 mt + row
+            {
+                const int mt = tid >> 5, hf = (tid >> 4) & 1, k = 16 * mt + (tid & 15);
                 const float gk = sm.gam[k];
                 float v[8];
 #pragma unroll
@@ -418,7 +418,7 @@ void prefill_kernel(const Ptrs p, const int L)
                 u32x4 pc[3];
                 split8(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}, pc);
 #pragma unroll
-                for (int q = 0; q < 3; ++q) sm.ktp[q][mt][hf][f & 15] = pc[q];
+                for (int q = 0; q < 3; ++q) sm.ktp[q][mt][hf][tid & 15] = pc[q];
             }
         }
         lds_barrier();
@@ -501,7 +501,7 @@ void prefill_kernel(const Ptrs p, const int L)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) dl[nt][kk] = sm.eg[4 * g4 + kk][ncol + 16 * nt + l16];
         {
-            const f32x4 p4 = lds4(&sm.P[l16][4 * g4]);
+            const f32x4 p4 = lds4(&sm.P[0][l16][4 * g4]) + lds4(&sm.P[1][l16][4 * g4]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
