@@ -155,3 +155,39 @@ def test_prefill_benchmark_shapes_sampled(orc, M, L, state_dtype):
         assert e_s <= tol_s, f"state ({m},{h}): {e_s:.3e}"
         assert e_o <= TOL_O, f"outputs ({m},{h}): {e_o:.3e}"
     say(f"prefill {M} x {L} tokens {state_dtype}, units {units}: state {worst_s:.3e} o {worst_o:.3e}")
+
+
+# Gate and write-strength extremes.  With dt_bias = +12 the bounded gate
+# saturates (sigmoid ~ 1, g ~ lb = -5 at every token), so a 16-token chunk
+# decays by e^-80 and its inverse decay reaches e^+80: the range the chunk
+# form relies on staying inside f32.  dt_bias = -40 gives g ~ 0 (alpha ~ 1,
+# no decay); beta logits of +-20 give beta ~ 1 and ~ 0.
+@pytest.mark.parametrize("case", ["saturated_gate", "no_decay", "beta_extremes"])
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+def test_prefill_gate_extremes(orc, case, state_dtype):
+    M, H, L, D = 2, 3, 53, 128
+    wl = kda_synth.custom(f"prefill_ext_{case}", M, H, D, steps=L, seed=11)
+    li = kda_synth.layer_inputs(wl, 0, DEV, state_dtype)
+    gp = kda_synth.gate_params(wl, 0, DEV)
+    x, f, bl = sequence(wl, L)
+    if case == "saturated_gate":
+        gp["dt_bias"] = torch.full_like(gp["dt_bias"], 12.0)
+    elif case == "no_decay":
+        gp["dt_bias"] = torch.full_like(gp["dt_bias"], -40.0)
+    else:
+        sign = torch.where(torch.arange(L, device=DEV) % 2 == 0, 1.0, -1.0)
+        bl = (20.0 * sign)[None, :, None].expand(M, L, H).to(torch.bfloat16).contiguous()
+    S, cs = li["state"], li["conv_state"]
+    o = torch.empty((M, L, H, D), dtype=torch.bfloat16, device=DEV)
+    S0, cs0 = host(S), host(cs)
+    kda_prefill_gated(S, x, li["conv_w"], cs, cs, f, gp["A_log"], gp["dt_bias"], bl, wl.scale, o)
+    torch.cuda.synchronize()
+    S_ref, cs_ref, o_ref = orc.sequence_gated(S0, host(x), host(li["conv_w"]), cs0, host(f), host(gp["A_log"]),
+                                              host(gp["dt_bias"]), host(bl), wl.scale)
+    assert torch.isfinite(S).all() and torch.isfinite(o.float()).all()
+    e_s = rel_err(host(S), S_ref)
+    e_o = max(rel_err(host(o[:, t]), o_ref[:, t]) for t in range(L))
+    say(f"prefill {case} {state_dtype}: state {e_s:.3e} o {e_o:.3e}")
+    assert np.array_equal(host(cs), cs_ref)
+    assert e_s <= (TOL_STATE_PREFILL if state_dtype == "f32" else 4e-3), f"state error {e_s:.3e}"
+    assert e_o <= TOL_O, f"output error {e_o:.3e}"
