@@ -113,3 +113,49 @@ def test_multi_empty():
                      e(2, 0, 3, 16), e(2, 0, 3), 0.25, e(2, 0, 3, 16, dt=torch.bfloat16))
     torch.cuda.synchronize()
     assert torch.equal(S, li["state"])
+
+
+# Fade extremes: alpha of exactly 1, a steep fade whose running product
+# underflows f32 within a few tokens, tokens with alpha 1e-25 or exactly 0 in
+# some rows, and alpha log-uniform over [1e-9, 1] -- over enough tokens to
+# cross many of the kernel's token chunks.  Any scheme that reorders or defers
+# the per-row fade must still match the oracle's plain recurrence on these.
+def fade_pattern(case, M, T, H, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    if case == "one":
+        a = torch.ones(M, T, H, D, dtype=torch.float64)
+    elif case == "steep":                  # C passes 2^-64 every few tokens
+        a = torch.full((M, T, H, D), 2.0 ** -12, dtype=torch.float64)
+    elif case == "tiny":                   # chunks whose own product underflows the range
+        a = torch.rand(M, T, H, D, generator=g, dtype=torch.float64) * 0.5 + 0.5
+        a[:, 3::7] = 1e-25
+    elif case == "zero":                   # some rows reset outright
+        a = torch.rand(M, T, H, D, generator=g, dtype=torch.float64) * 0.5 + 0.5
+        a[:, 5::9, :, ::3] = 0.0
+    else:                                  # log-uniform over [1e-9, 1]
+        a = torch.exp(-torch.rand(M, T, H, D, generator=g, dtype=torch.float64) * (9 * np.log(10)))
+    return a.float().to(DEV).contiguous()
+
+
+@pytest.mark.parametrize("case", ["one", "steep", "tiny", "zero", "loguniform"])
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,H,D,T", [(2, 3, 128, 40), (2, 2, 64, 33), (1, 2, 16, 29)])
+def test_multi_fade_extremes(orc, M, H, D, T, state_dtype, case):
+    wl = kda_synth.custom(f"multi_fade_{M}_{H}_{D}", M, H, D, steps=T)
+    li = kda_synth.layer_inputs(wl, 0, DEV, state_dtype)
+    S, w, cs = li["state"], li["conv_w"], li["conv_state"]
+    ins = tokens(wl, 0, T)
+    alpha = fade_pattern(case, M, T, H, D, seed=D + T)
+    o = torch.empty((M, T, H, D), dtype=torch.bfloat16, device=DEV)
+    S0, cs0 = host(S), host(cs)
+    kda_decode_multi(S, ins["x"], w, cs, cs, alpha, ins["beta"], wl.scale, o)
+    torch.cuda.synchronize()
+    S_ref, cs_ref, o_ref = orc.decode_multi(S0, host(ins["x"]), host(w), cs0, host(alpha), host(ins["beta"]),
+                                            wl.scale)
+    assert torch.isfinite(S).all() and torch.isfinite(o.float()).all()
+    assert np.array_equal(host(cs), cs_ref)
+    e_s = rel_err(host(S), S_ref)
+    e_o = max(rel_err(host(o[:, t]), o_ref[:, t]) for t in range(T))
+    say(f"multi fade {case} ({M},{H},{D}) T={T} {state_dtype}: state {e_s:.3e} o {e_o:.3e}")
+    assert e_s <= tol_state(state_dtype), f"state error {e_s:.3e}"
+    assert e_o <= TOL_O, f"output error {e_o:.3e}"
