@@ -286,14 +286,19 @@ def measure_prefill(M, L, state_dtype, steps, warmup, H=64, D=128):
     vp = ctypes.c_void_p
     sdt = kda.KDA_STATE_F32 if state_dtype == "f32" else kda.KDA_STATE_BF16
     stream = torch.cuda.Stream()
-    args = (L, M, H, D, sdt, vp(li["state"].data_ptr()), vp(seq["x"].data_ptr()),
-            vp(li["conv_w"].data_ptr()), vp(li["conv_state"].data_ptr()), vp(li["conv_state"].data_ptr()),
-            vp(seq["f"].data_ptr()), vp(gp["A_log"].data_ptr()), vp(gp["dt_bias"].data_ptr()),
-            vp(seq["beta_logit"].data_ptr()), ctypes.c_float(-5.0), ctypes.c_float(wl.scale),
-            vp(o.data_ptr()), vp(stream.cuda_stream))
+    # the conv state alternates between two buffers (conv_in != conv_out):
+    # with few heads the library then splits each head over two workgroups
+    cs = (li["conv_state"], li["conv_state"].clone())
+    args = [(L, M, H, D, sdt, vp(li["state"].data_ptr()), vp(seq["x"].data_ptr()),
+             vp(li["conv_w"].data_ptr()), vp(cs[i].data_ptr()), vp(cs[1 - i].data_ptr()),
+             vp(seq["f"].data_ptr()), vp(gp["A_log"].data_ptr()), vp(gp["dt_bias"].data_ptr()),
+             vp(seq["beta_logit"].data_ptr()), ctypes.c_float(-5.0), ctypes.c_float(wl.scale),
+             vp(o.data_ptr()), vp(stream.cuda_stream)) for i in (0, 1)]
+    calls = [0]
 
     def launch():
-        rc = lib.kda_prefill_gated(*args)
+        rc = lib.kda_prefill_gated(*args[calls[0] & 1])
+        calls[0] += 1
         if rc:
             raise RuntimeError(f"kda_prefill_gated returned {rc}")
 
@@ -312,7 +317,7 @@ def measure_prefill(M, L, state_dtype, steps, warmup, H=64, D=128):
     flops = PREFILL_FLOPS_PER_CHUNK_HEAD * M * H * L // PREFILL_CHUNK
     nbytes = (M * (L * PREFILL_TOKEN_BYTES + PREFILL_STREAM_BYTES) + PREFILL_LAYER_BYTES
               + 2 * wl.state_bytes(state_dtype))
-    del li, gp, seq, o
+    del li, gp, seq, o, cs
     torch.cuda.empty_cache()
     return {"workload": f"prefill_m{M}_l{L}", "M": M, "L": L, "H": H, "D": D,
             "state_dtype": state_dtype, "entry_point": "kda_prefill_gated", "launch": "eager",

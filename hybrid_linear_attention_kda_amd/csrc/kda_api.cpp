@@ -324,7 +324,7 @@ int kda_prefill_gated(int L, int M, int H, int D, int state_dtype, void* state, 
         if (overlap(rco, inputs[i])) return KDA_ERR_ALIAS;
     }
     kda::StepArgs a{};
-    a.M = M; a.H = H; a.D = D; a.T = L; a.state_dtype = state_dtype; a.nsplit = 1;
+    a.M = M; a.H = H; a.D = D; a.T = L; a.state_dtype = state_dtype; a.nsplit = 0;
     a.state = state; a.x = x_qkv; a.conv_w = conv_w; a.conv_in = conv_in; a.conv_out = conv_out;
     a.fgate = f_gate; a.A_log = A_log; a.dt_bias = dt_bias; a.beta_logit = beta_logit;
     a.gate_kind = KDA_GATE_BOUNDED; a.lower_bound = gate_lower_bound; a.scale = scale; a.o = o;

@@ -222,28 +222,33 @@ __device__ __forceinline__ void solve_column(float (&cv)[PC], const float (*Z)[P
 
 }  // namespace
 
-// One workgroup per (stream, head); x [M][L][3][H*D], fgate [M][L][H*D],
-// blogit [M][L][H], o [M][L][H][D].
-template <typename TS>
+// NS workgroups per (stream, head), each owning 128 / NS value columns of
+// the state (the columns evolve independently: only the state products,
+// the update and the outputs are split; the inputs, A, P and the solves are
+// computed by each).  x [M][L][3][H*D], fgate [M][L][H*D], blogit [M][L][H],
+// o [M][L][H][D].
+template <typename TS, int NS>
 __global__ __launch_bounds__(PNT, 2)
 void prefill_kernel(const Ptrs p, const int L)
 {
+    static_assert(NS == 1 || NS == 2, "one or two workgroups per head");
+    constexpr int NTW = 2 / NS;                        // 16-column tiles per wave
     __shared__ PrefillSmem sm;
-    const int unit = (int)blockIdx.x;
+    const int unit = (int)blockIdx.x / NS, split = (int)blockIdx.x - unit * NS;
     const int m = unit / p.H, h = unit - m * p.H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform: roles branch on it
     const int l16 = lane & 15, g4 = lane >> 4;
     const size_t HD = (size_t)p.H * PD, C3 = 3 * HD;
-    const int ncol = 32 * wv;                          // this wave's value columns
+    const int ncol = (PD / NS) * split + 16 * NTW * wv;   // this wave's value columns
 
     // ---- the state, in the MFMA output layout ----
     TS* const st = static_cast<TS*>(p.state) + (size_t)unit * PD * PD;
-    float S[8][2][4];
+    float S[8][NTW][4];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 S[mt][nt][r] = load_state_elem(st + (size_t)(16 * mt + 4 * g4 + r) * PD + ncol + 16 * nt + l16);
@@ -450,16 +455,18 @@ void prefill_kernel(const Ptrs p, const int L)
         // registers) are the B fragment; the A fragments (-W and Gamma . q^
         // of token lane % 16 at the same rows) come split from LDS.  Six bf16
         // products per pair of split operands.
-        f32x4 dacc[2], oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 dacc[NTW], oacc[NTW];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NTW; ++nt) {
+            oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < 4; ++r) dacc[nt][r] = sm.vv[4 * g4 + r][ncol + 16 * nt + l16];
+        }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            u32x4 sb[2][3], wp[3], gp[3];
+            u32x4 sb[NTW][3], wp[3], gp[3];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NTW; ++nt)
                 split8(f32x4{S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3]},
                        f32x4{S[2 * kb + 1][nt][0], S[2 * kb + 1][nt][1], S[2 * kb + 1][nt][2], S[2 * kb + 1][nt][3]},
                        sb[nt]);
@@ -469,7 +476,7 @@ void prefill_kernel(const Ptrs p, const int L)
 #pragma unroll
             for (int pr = 0; pr < 6; ++pr)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+                for (int nt = 0; nt < NTW; ++nt) {
                     dacc[nt] = mfma_bf16(wp[PAIR_A[pr]], sb[nt][PAIR_B[pr]], dacc[nt]);
                     oacc[nt] = mfma_bf16(gp[PAIR_A[pr]], sb[nt][PAIR_B[pr]], oacc[nt]);
                 }
@@ -478,7 +485,7 @@ void prefill_kernel(const Ptrs p, const int L)
         // where q^ and 1 / Gamma were: this lane's 4 tokens 4 (lane / 16) + r
         // are half of the fragment of token half (lane / 32)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.eg[4 * g4 + r][ncol + 16 * nt + l16] = dacc[nt][r];
             uint32_t p0a, p1a, p2a, p0b, p1b, p2b;
@@ -495,15 +502,15 @@ void prefill_kernel(const Ptrs p, const int L)
 
         // ---- 5. O = (Gamma . Q) S + P Delta; S' = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta ----
         // contraction over tokens: the k slot lane / 16 is token 4 (lane / 16) + kk
-        float dl[2][4];
+        float dl[NTW][4];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) dl[nt][kk] = sm.eg[4 * g4 + kk][ncol + 16 * nt + l16];
         {
             const f32x4 p4 = lds4(&sm.P[0][l16][4 * g4]) + lds4(&sm.P[1][l16][4 * g4]);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) oacc[nt] = mfma16(p4[kk], dl[nt][kk], oacc[nt]);
                 const int col = ncol + 16 * nt + l16;
@@ -520,11 +527,11 @@ void prefill_kernel(const Ptrs p, const int L)
         // takes pair 2 m + s, tokens 8 hh .. 8 hh + 7
         {
             const int hh = g4 & 1, sel = g4 >> 1;
-            u32x4 db[3][2];
+            u32x4 db[3][NTW];
 #pragma unroll
             for (int mm = 0; mm < 3; ++mm)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < NTW; ++nt)
                     db[mm][nt] = sm.dp[sel ? PAIR_B[2 * mm + 1] : PAIR_B[2 * mm]][wv][nt][hh][l16];
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
@@ -533,7 +540,7 @@ void prefill_kernel(const Ptrs p, const int L)
 #pragma unroll
                 for (int mm = 0; mm < 3; ++mm) ka[mm] = sm.ktp[sel ? PAIR_A[2 * mm + 1] : PAIR_A[2 * mm]][mt][hh][l16];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+                for (int nt = 0; nt < NTW; ++nt) {
                     f32x4 acc = {S[mt][nt][0] * gm.x, S[mt][nt][1] * gm.y, S[mt][nt][2] * gm.z, S[mt][nt][3] * gm.w};
 #pragma unroll
                     for (int mm = 0; mm < 3; ++mm) acc = mfma_bf16(ka[mm], db[mm][nt], acc);
@@ -553,14 +560,16 @@ void prefill_kernel(const Ptrs p, const int L)
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 store_state_elem(st + so + (16 * mt + r) * PD + 16 * nt, S[mt][nt][r]);
     // conv state after the sequence: the raw inputs of positions L-3, L-2,
     // L-1, where a position < 0 is a cached tap (read before this lane
-    // overwrites it: conv_out may be conv_in, and each lane owns its channels)
-    if (wv < 3) {
+    // overwrites it: conv_out may be conv_in, and each lane owns its channels;
+    // with NS = 2 the first workgroup of the head writes it, and the host
+    // requires conv_out != conv_in, since the other one reads conv_in)
+    if (wv < 3 && split == 0) {
         uint32_t nt3[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -574,14 +583,27 @@ void prefill_kernel(const Ptrs p, const int L)
     }
 }
 
+// Two workgroups per head when the heads alone would leave more than half
+// of the CUs idle (the duplicated input, A, P and solve work then costs
+// nothing but otherwise idle CUs) and conv_out is a buffer of its own.
 hipError_t launch_prefill(const StepArgs& a) {
     if (a.D != PD) return hipErrorInvalidValue;
     Ptrs p = make_ptrs(a);
     int L = a.T;
     void* args[] = {(void*)&p, (void*)&L};
-    const void* fn = a.state_dtype == 0 ? reinterpret_cast<const void*>(&prefill_kernel<float>)
-                                        : reinterpret_cast<const void*>(&prefill_kernel<uint16_t>);
-    return hipLaunchKernel(fn, dim3((unsigned)(a.M * a.H)), dim3(PNT), args, 0, (hipStream_t)a.stream);
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long units = (long)a.M * a.H;
+    const bool two = a.nsplit == 0 && a.conv_out != a.conv_in && 2 * units <= ncu;   // nsplit 0: choose
+    const bool f32 = a.state_dtype == 0;
+    const void* fn = two ? (f32 ? reinterpret_cast<const void*>(&prefill_kernel<float, 2>)
+                                : reinterpret_cast<const void*>(&prefill_kernel<uint16_t, 2>))
+                         : (f32 ? reinterpret_cast<const void*>(&prefill_kernel<float, 1>)
+                                : reinterpret_cast<const void*>(&prefill_kernel<uint16_t, 1>));
+    return hipLaunchKernel(fn, dim3((unsigned)(units * (two ? 2 : 1))), dim3(PNT), args, 0, (hipStream_t)a.stream);
 }
 
 }  // namespace kda

@@ -131,11 +131,12 @@ def test_prefill_benchmark_shapes_sampled(orc, M, L, state_dtype):
     gp = kda_synth.gate_params(wl, 0, DEV)
     seq = kda_synth.sequence_inputs(wl, 0, L, DEV)
     S, cs = li["state"], li["conv_state"]
+    cout = torch.empty_like(cs)                  # as bench.py launches it: conv state ping-pong
     o = torch.empty((M, L, H, D), dtype=torch.bfloat16, device=DEV)
     units = sorted({(0, 0), (M - 1, H - 1), (M // 2, 17), (min(1, M - 1), 40)})
     S0 = {u: host(S[u[0], u[1]]) for u in units}
     cs0 = host(cs)
-    kda_prefill_gated(S, seq["x"], li["conv_w"], cs, cs, seq["f"], gp["A_log"], gp["dt_bias"],
+    kda_prefill_gated(S, seq["x"], li["conv_w"], cs, cout, seq["f"], gp["A_log"], gp["dt_bias"],
                       seq["beta_logit"], wl.scale, o)
     torch.cuda.synchronize()
     cw = host(li["conv_w"]).reshape(3, H, D, 4)
@@ -144,11 +145,13 @@ def test_prefill_benchmark_shapes_sampled(orc, M, L, state_dtype):
     for (m, h) in units:
         sl = slice(h * D, (h + 1) * D)
         xu = host(seq["x"][m, :, :, sl]).reshape(1, L, 3, D)
-        S_ref, _, o_ref = orc.sequence_gated(
+        S_ref, cs_ref, o_ref = orc.sequence_gated(
             S0[(m, h)][None, None], xu, cw[:, h].reshape(3 * D, 4),
             cs0[m].reshape(3, 3, H, D)[:, :, h].reshape(1, 3, 3 * D),
             host(seq["f"][m, :, sl])[None], host(gp["A_log"][h:h + 1]), host(gp["dt_bias"][sl]),
             host(seq["beta_logit"][m, :, h:h + 1])[None], wl.scale)
+        assert np.array_equal(host(cout[m]).reshape(3, 3, H, D)[:, :, h].reshape(3, 3 * D), cs_ref[0]), \
+            f"conv state ({m},{h})"
         e_s = rel_err(host(S[m, h]), S_ref[0, 0])
         e_o = rel_err(host(o[m, :, h]), o_ref[0, :, 0])
         worst_s, worst_o = max(worst_s, e_s), max(worst_o, e_o)
@@ -191,3 +194,30 @@ def test_prefill_gate_extremes(orc, case, state_dtype):
     assert np.array_equal(host(cs), cs_ref)
     assert e_s <= (TOL_STATE_PREFILL if state_dtype == "f32" else 4e-3), f"state error {e_s:.3e}"
     assert e_o <= TOL_O, f"output error {e_o:.3e}"
+
+
+# With conv_out apart from conv_in and few heads (2 M H <= the CU count), the
+# library runs two workgroups per head, each owning half of the value
+# columns; their arithmetic per column is the one-workgroup kernel's, in the
+# same order, so the results must be bit-identical to an in-place call (which
+# always runs one workgroup per head).
+@pytest.mark.parametrize("M,H,L,state_dtype", [(1, 64, 300, "f32"), (2, 3, 64, "bf16"), (1, 1, 1, "f32"),
+                                               (2, 64, 40, "f32"), (1, 5, 35, "bf16"), (3, 2, 17, "f32")])
+def test_prefill_split_matches_single(M, H, L, state_dtype):
+    wl = kda_synth.custom(f"prefill_split_{M}_{H}_{L}", M, H, 128, steps=L, seed=3)
+    li = kda_synth.layer_inputs(wl, 0, DEV, state_dtype)
+    gp = kda_synth.gate_params(wl, 0, DEV)
+    x, f, bl = sequence(wl, L)
+    S1, cs1 = li["state"].clone(), li["conv_state"].clone()
+    S2, cs2 = li["state"].clone(), li["conv_state"].clone()
+    cout2 = torch.empty_like(cs2)
+    o1 = torch.empty((M, L, H, 128), dtype=torch.bfloat16, device=DEV)
+    o2 = torch.empty_like(o1)
+    kda_prefill_gated(S1, x, li["conv_w"], cs1, cs1, f, gp["A_log"], gp["dt_bias"], bl, wl.scale, o1)
+    kda_prefill_gated(S2, x, li["conv_w"], cs2, cout2, f, gp["A_log"], gp["dt_bias"], bl, wl.scale, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(S1, S2), "state"
+    assert torch.equal(o1, o2), "outputs"
+    assert torch.equal(cs1, cout2), "conv state"
+    assert torch.equal(cs2, li["conv_state"]), "conv_in untouched"
+    say(f"prefill split ({M},{H},L={L}) {state_dtype}: bit-identical")
