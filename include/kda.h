@@ -228,6 +228,12 @@ int kda_decode_multi(int T, int M, int H, int D, int state_dtype,
  *
  * One workgroup per (stream, head) sweeps its chunks in order, so M*H
  * should be at least the device's compute-unit count for a full device.
+ * When 2*M*H is at most that count and conv_out is not conv_in, two
+ * workgroups share each head, each owning half of the value columns (the
+ * columns of the state evolve independently); the results are bit-identical
+ * to the one-workgroup form.  In place (conv_out == conv_in) the kernel
+ * always runs one workgroup per head, as the second one would read cached
+ * taps the first has overwritten.
  * Results agree with the token-by-token recurrence to the rounding of the
  * reordered f32 arithmetic (see the tests), not bit for bit.  Returns a
  * KDA_* status (KDA_ERR_SHAPE for D != 128, KDA_ERR_ARG for a lower bound
