@@ -449,8 +449,8 @@ template <typename TS, int D, int NWAVES, int VEC, int RMAP, int TCMAX = 16>
 struct MultiGeo {
     typedef Geo<TS, D, 1, NWAVES, VEC, RMAP> G;
     static constexpr int NGT = 3 * D / 4;            // channel groups of one token
-    static constexpr int TC = G::NT / NGT < TCMAX ? G::NT / NGT : TCMAX;   // tokens per chunk
-    static_assert(TC >= 1, "one token's channel groups must fit the workgroup");
+    static constexpr int TC = TCMAX;                 // tokens per chunk
+    static constexpr int ITEMS = (TC * NGT + G::NT - 1) / G::NT;   // (token, group) items per thread
     static constexpr int ZW = 3 * D;                 // conv outputs of one token: q, k, v
 };
 
@@ -473,34 +473,62 @@ __device__ __forceinline__ u32x2 seq_input(const Ptrs& p, int T, int m, size_t C
 }
 
 // Conv, alpha, beta and norms of tokens [c0, c0 + n) into LDS.
-template <class MG, int D>
+template <class MG, int D, bool ALL = true>
 __device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, int c0, int n,
                                             MultiSmem<MG, D>& sm) {
     typedef typename MG::G G;
+    constexpr int IT = MG::ITEMS;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
-    const int j = tid / MG::NGT, g = tid - j * MG::NGT;
-    if (j < n) {
-        const int tok = c0 + j;
-        const size_t ch = group_channel<G, D>(g, h, 0, HD);
-        const u32x2 xv = seq_input(p, T, m, C3, ch, tok);
-        const u32x2 t2 = seq_input(p, T, m, C3, ch, tok - 1);
-        const u32x2 t1 = seq_input(p, T, m, C3, ch, tok - 2);
-        const u32x2 t0 = seq_input(p, T, m, C3, ch, tok - 3);
-        const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
-        const u32x4 w01 = wp[0], w23 = wp[1];
-        const size_t mt = (size_t)m * T + tok;
-        f32x4 av;
-        if (g < D / 4) av = *reinterpret_cast<const f32x4*>(p.alpha + mt * HD + (size_t)h * D + 4 * g);
-        float bv = 0.0f;
-        if (g == 0) bv = p.beta[mt * p.H + h];
-        reinterpret_cast<f32x4*>(sm.z[j])[g] =
-            f32x4{conv_silu(u32x2{w01.x, w01.y}, bf16_lo(t0.x), bf16_lo(t1.x), bf16_lo(t2.x), bf16_lo(xv.x)),
-                  conv_silu(u32x2{w01.z, w01.w}, bf16_hi(t0.x), bf16_hi(t1.x), bf16_hi(t2.x), bf16_hi(xv.x)),
-                  conv_silu(u32x2{w23.x, w23.y}, bf16_lo(t0.y), bf16_lo(t1.y), bf16_lo(t2.y), bf16_lo(xv.y)),
-                  conv_silu(u32x2{w23.z, w23.w}, bf16_hi(t0.y), bf16_hi(t1.y), bf16_hi(t2.y), bf16_hi(xv.y))};
-        if (g < D / 4) reinterpret_cast<f32x4*>(sm.a[j])[g] = av;
-        if (g == 0) sm.b[j] = bv;
+    // ALL: every item's loads go out before any is used (the chunk waits
+    // for memory once); otherwise item by item, which holds a third of the
+    // registers (chunks after the first, when the state is in registers)
+    u32x2 xv[IT], t0[IT], t1[IT], t2[IT];
+    u32x4 w01[IT], w23[IT];
+    f32x4 av[IT];
+    float bv[IT];
+    auto load_item = [&](int k) {
+        const int idx = tid + k * G::NT, j = idx / MG::NGT, g = idx - j * MG::NGT;
+        if (j < n) {
+            const int tok = c0 + j;
+            const size_t ch = group_channel<G, D>(g, h, 0, HD);
+            xv[k] = seq_input(p, T, m, C3, ch, tok);
+            t2[k] = seq_input(p, T, m, C3, ch, tok - 1);
+            t1[k] = seq_input(p, T, m, C3, ch, tok - 2);
+            t0[k] = seq_input(p, T, m, C3, ch, tok - 3);
+            const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
+            w01[k] = wp[0];
+            w23[k] = wp[1];
+            const size_t mt = (size_t)m * T + tok;
+            if (g < D / 4) av[k] = *reinterpret_cast<const f32x4*>(p.alpha + mt * HD + (size_t)h * D + 4 * g);
+            if (g == 0) bv[k] = p.beta[mt * p.H + h];
+        }
+    };
+    auto conv_item = [&](int k) {
+        const int idx = tid + k * G::NT, j = idx / MG::NGT, g = idx - j * MG::NGT;
+        if (j < n) {
+            const u32x4 wa = w01[k], wb = w23[k];
+            const u32x2 x0 = t0[k], x1 = t1[k], x2 = t2[k], x3 = xv[k];
+            reinterpret_cast<f32x4*>(sm.z[j])[g] =
+                f32x4{conv_silu(u32x2{wa.x, wa.y}, bf16_lo(x0.x), bf16_lo(x1.x), bf16_lo(x2.x), bf16_lo(x3.x)),
+                      conv_silu(u32x2{wa.z, wa.w}, bf16_hi(x0.x), bf16_hi(x1.x), bf16_hi(x2.x), bf16_hi(x3.x)),
+                      conv_silu(u32x2{wb.x, wb.y}, bf16_lo(x0.y), bf16_lo(x1.y), bf16_lo(x2.y), bf16_lo(x3.y)),
+                      conv_silu(u32x2{wb.z, wb.w}, bf16_hi(x0.y), bf16_hi(x1.y), bf16_hi(x2.y), bf16_hi(x3.y))};
+            if (g < D / 4) reinterpret_cast<f32x4*>(sm.a[j])[g] = av[k];
+            if (g == 0) sm.b[j] = bv[k];
+        }
+    };
+    if constexpr (ALL) {
+#pragma unroll
+        for (int k = 0; k < IT; ++k) load_item(k);
+#pragma unroll
+        for (int k = 0; k < IT; ++k) conv_item(k);
+    } else {
+#pragma unroll 1
+        for (int k = 0; k < IT; ++k) {
+            load_item(k);
+            conv_item(k);
+        }
     }
     lds_barrier();
     // one wave per token: the L2 norms of q and k and k^.q^
@@ -609,7 +637,7 @@ __device__ __forceinline__ void multi_token(float (&sreg)[MG::G::RPL][MG::G::IO_
 // One workgroup per (stream, head), T >= 1 tokens; x [M][T][3][H*D],
 // alpha [M][T][H][D], beta [M][T][H], o [M][T][H][D].
 template <typename TS, int D, int NWAVES, int VEC, int RMAP, int TCMAX = 16>
-__global__ __launch_bounds__(NWAVES * 64)
+__global__ __launch_bounds__(NWAVES * 64, D == 128 ? 3 : 1)   // D = 128: 3 workgroups per CU
 void decode_multi_kernel(const Ptrs p, const int units, const int T)
 {
     typedef MultiGeo<TS, D, NWAVES, VEC, RMAP, TCMAX> MG;
@@ -621,18 +649,16 @@ void decode_multi_kernel(const Ptrs p, const int units, const int T)
     const int m = unit / p.H, h = unit - m * p.H;
     const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
 
-    // the state loads go out first; the first chunk's small loads overlap them
+    // the first chunk's inputs are computed before the state is requested,
+    // so its items and the in-flight state never hold registers together
     TS* const st = static_cast<TS*>(p.state) + (size_t)unit * D * D + cg * G::IO_VEC;
-    typename G::raw_t raw[G::RPL];
-#pragma unroll
-    for (int r = 0; r < G::RPL; ++r) raw[r] = G::IO::load(st + (size_t)G::row(wv, rw, r) * D);
-    __builtin_amdgcn_sched_barrier(0);
     float sreg[G::RPL][G::IO_VEC];
-
-    // the first chunk is peeled: the raw state registers die at the unpack
     {
         const int n = min(MG::TC, T);
         multi_chunk<MG, D>(p, T, m, h, 0, n, sm);
+        typename G::raw_t raw[G::RPL];
+#pragma unroll
+        for (int r = 0; r < G::RPL; ++r) raw[r] = G::IO::load(st + (size_t)G::row(wv, rw, r) * D);
 #pragma unroll
         for (int r = 0; r < G::RPL; ++r) G::IO::unpack(raw[r], sreg[r]);
         for (int t = 0; t < n; ++t) multi_token<TS, MG, D>(sreg, p, T, m, h, t, t, sm);
@@ -641,7 +667,7 @@ void decode_multi_kernel(const Ptrs p, const int units, const int T)
     }
     for (int c0 = MG::TC; c0 < T; c0 += MG::TC) {
         const int n = min(MG::TC, T - c0);
-        multi_chunk<MG, D>(p, T, m, h, c0, n, sm);
+        multi_chunk<MG, D, false>(p, T, m, h, c0, n, sm);
         for (int t = 0; t < n; ++t) multi_token<TS, MG, D>(sreg, p, T, m, h, c0 + t, t, sm);
         lds_barrier();
     }
@@ -770,13 +796,13 @@ static hipError_t dispatch(const StepArgs& a) {
     }
 }
 
-template <typename TS, int D, int NWAVES, int VEC, int RMAP>
+template <typename TS, int D, int NWAVES, int VEC, int RMAP, int TC>
 static hipError_t launch_multi(const StepArgs& a) {
     Ptrs p = make_ptrs(a);
     int units = a.M * a.H;
     int T = a.T;
     void* args[] = {(void*)&p, (void*)&units, (void*)&T};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_multi_kernel<TS, D, NWAVES, VEC, RMAP>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_multi_kernel<TS, D, NWAVES, VEC, RMAP, TC>),
                            dim3((unsigned)units), dim3(NWAVES * 64), args, 0, (hipStream_t)a.stream);
 }
 
@@ -784,14 +810,14 @@ static hipError_t launch_multi(const StepArgs& a) {
 hipError_t launch_decode_multi(const StepArgs& a) {
     const bool f32 = a.state_dtype == 0;
     switch (a.D) {
-    case 16: return f32 ? launch_multi<float, 16, 1, 4, 0>(a) : launch_multi<uint16_t, 16, 1, 4, 0>(a);
-    case 32: return f32 ? launch_multi<float, 32, 1, 4, 0>(a) : launch_multi<uint16_t, 32, 1, 8, 0>(a);
-    case 64: return f32 ? launch_multi<float, 64, 2, 4, 0>(a) : launch_multi<uint16_t, 64, 2, 8, 0>(a);
+    case 16: return f32 ? launch_multi<float, 16, 1, 4, 0, 5>(a) : launch_multi<uint16_t, 16, 1, 4, 0, 5>(a);
+    case 32: return f32 ? launch_multi<float, 32, 1, 4, 0, 2>(a) : launch_multi<uint16_t, 32, 1, 8, 0, 2>(a);
+    case 64: return f32 ? launch_multi<float, 64, 2, 4, 0, 2>(a) : launch_multi<uint16_t, 64, 2, 8, 0, 2>(a);
     case 128:
         // 4 waves per head (16 or 8 rows per lane), each wave a band of rows:
         // the token loop is latency-bound, so more heads per CU beat more
         // waves per head (measured)
-        return f32 ? launch_multi<float, 128, 4, 4, 1>(a) : launch_multi<uint16_t, 128, 4, 8, 1>(a);
+        return f32 ? launch_multi<float, 128, 4, 4, 1, 8>(a) : launch_multi<uint16_t, 128, 4, 8, 1, 8>(a);
     default: return hipErrorInvalidValue;
     }
 }
