@@ -438,12 +438,15 @@ void decode_kernel(const Ptrs p, const int units)
 //
 // Only the fade, the reductions and the rank-1 write depend on the state.
 // Everything else (conv + SiLU, the norms, alpha, beta) is computed for a
-// chunk of TC tokens at once: lane (j, g) of the workgroup computes the 4
-// channels of group g for token j of the chunk, reading the three previous
-// raw inputs of those channels (from x, or from the conv state for the first
-// three tokens); one wave per token then forms its norms.  The serial loop
-// over the chunk's tokens then touches only LDS and the state registers, with
-// two barriers per token.
+// chunk of TC tokens at once: the workgroup's threads take the chunk's
+// (token j, channel group g) items in turn, each computing the 4 channels of
+// group g for token j from the three previous raw inputs of those channels
+// (from x, or from the conv state for the first three tokens); one wave per
+// token then forms its norms.  The serial loop over the chunk's tokens then
+// touches only LDS and the state registers, with two barriers per token.
+// The first chunk is computed before the state is requested: a wave's loads
+// complete in order, so inputs requested after the state would wait for it,
+// and requested together with it they would hold registers beside it.
 
 template <typename TS, int D, int NWAVES, int VEC, int RMAP, int TCMAX = 16>
 struct MultiGeo {
