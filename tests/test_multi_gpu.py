@@ -159,3 +159,21 @@ def test_multi_fade_extremes(orc, M, H, D, T, state_dtype, case):
     say(f"multi fade {case} ({M},{H},{D}) T={T} {state_dtype}: state {e_s:.3e} o {e_o:.3e}")
     assert e_s <= tol_state(state_dtype), f"state error {e_s:.3e}"
     assert e_o <= TOL_O, f"output error {e_o:.3e}"
+
+
+# Token counts around the D = 128 kernel's 8-token chunks: one chunk plus one
+# token, two full chunks, two plus one, and a ragged third.
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [9, 16, 17, 23])
+def test_multi_chunk_boundaries(orc, T, state_dtype):
+    M, H, D = 2, 3, 128
+    wl = kda_synth.custom(f"multi_bound_{T}", M, H, D, steps=T)
+    S0, cs0, li, ins, S, cout, o = run_multi(wl, state_dtype, T, inplace=False)
+    S_ref, cs_ref, o_ref = orc.decode_multi(S0, host(ins["x"]), host(li["conv_w"]), cs0,
+                                            host(ins["alpha"]), host(ins["beta"]), wl.scale)
+    assert np.array_equal(host(cout), cs_ref), "conv state after T tokens"
+    e_s = rel_err(host(S), S_ref)
+    e_o = max(rel_err(host(o[:, t]), o_ref[:, t]) for t in range(T))
+    say(f"multi chunk boundary T={T} {state_dtype}: state {e_s:.3e} o {e_o:.3e}")
+    assert e_s <= tol_state(state_dtype), f"state error {e_s:.3e}"
+    assert e_o <= TOL_O, f"output error {e_o:.3e}"
