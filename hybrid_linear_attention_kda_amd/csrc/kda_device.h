@@ -91,6 +91,37 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// x + (x of lane l ^ OFF).  OFF = 16 and 32 use gfx950's row and half-wave
+// swaps on the VALU (v_permlane16_swap / v_permlane32_swap: swapping x with
+// itself leaves the values of the two partner lanes in the two results);
+// other offsets go through the LDS crossbar.  IEEE addition commutes, so
+// each lane gets the bits of x[l] + x[l ^ OFF] either way.
+template <int OFF>
+__device__ __forceinline__ float xor_add(float x) {
+    if constexpr (OFF == 32) {
+        const unsigned b = __float_as_uint(x);
+        const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else if constexpr (OFF == 16) {
+        const unsigned b = __float_as_uint(x);
+        const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        return x + __shfl_xor(x, OFF, 64);
+    }
+}
+
+// Sum over the lanes that differ from this one in lane-index bits
+// log2(FROM) and up (FROM a power of two), lowest bit first.
+template <int FROM>
+__device__ __forceinline__ float xor_reduce_from(float x) {
+    if constexpr (FROM >= 64) {
+        return x;
+    } else {
+        return xor_reduce_from<2 * FROM>(xor_add<FROM>(x));
+    }
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);

@@ -544,9 +544,9 @@ __device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, 
             skk = fmaf(kv, kv, skk);
             sqk = fmaf(qv, kv, sqk);
         }
-        sqq = wave_sum(sqq);
-        skk = wave_sum(skk);
-        sqk = wave_sum(sqk);
+        sqq = xor_reduce_from<1>(sqq);
+        skk = xor_reduce_from<1>(skk);
+        sqk = xor_reduce_from<1>(sqk);
         if (lane == 0) {
             const float rq = p.scale * rsqrtf(sqq + 1e-6f), rk = rsqrtf(skk + 1e-6f);
             sm.rq[t] = rq;
@@ -585,13 +585,12 @@ __device__ __forceinline__ void multi_token(float (&sreg)[MG::G::RPL][MG::G::IO_
             wq[e] = fmaf(sv, qq, wq[e]);
         }
     }
+    // lanes that share columns differ in the bits above log2(CG); the token
+    // loop is latency-bound, so the half-wave and row steps use the VALU swaps
 #pragma unroll
-    for (int off = CG; off < 64; off <<= 1) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            u[e] += __shfl_xor(u[e], off, 64);
-            wq[e] += __shfl_xor(wq[e], off, 64);
-        }
+    for (int e = 0; e < VEC; ++e) {
+        u[e] = xor_reduce_from<CG>(u[e]);
+        wq[e] = xor_reduce_from<CG>(wq[e]);
     }
 
     float d[VEC];
