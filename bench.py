@@ -35,7 +35,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "decode_kernel_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "hybrid_linear_attention_kda_amd", "csrc", "kda_kernels.hip")
+# the sources the decode kernel is compiled from (the stored counter traffic
+# is reported only while they are unchanged)
+KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_linear_attention_kda_amd", "csrc", n)
+                  for n in ("kda_kernels.hip", "kda_device.h")]
 METRIC = "KDA decode state GB/s + ms/layer at M=8,32 (FP32/BF16 state), % HBM peak"
 
 # algorithmic bytes besides the state, (per stream, per layer): the plain
@@ -73,8 +76,11 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 class Model:
@@ -612,8 +618,9 @@ def main():
         "replay_bitwise_equal": head["replay_bitwise_equal"],
         "stream_ceiling": None if ceiling is None else {
             "rmw_GBps": ceiling["rmw"], "copy_GBps": ceiling["copy"],
-            "kernel": "kda_probe_rmw / kda_probe_copy: 512 threads, one 16-byte non-temporal "
-                      "chunk per lane, one launch per 128 MiB layer chunk, 34 chunks",
+            "kernel": "kda_probe_rmw / kda_probe_copy: 512 threads, one 16-byte chunk per lane "
+                      "(non-temporal load, non-temporal agent-scope store), one launch per "
+                      "128 MiB layer chunk, 34 chunks",
             "decode_alg_over_rmw": achieved / ceiling["rmw"]},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -128,6 +128,27 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Stores with agent scope (sc1) as well as the non-temporal hint.  On MI355X
+// an in-place 16-byte stream over 128 MiB runs at 6.56 TB/s with them
+// against 6.41 TB/s with non-temporal stores alone (non-temporal loads
+// either way), but a launch of a single round of workgroups per CU takes
+// longer to drain its last such stores, so the launch code chooses per grid
+// size.  hipcc exposes cache-policy bits beyond the non-temporal one only on
+// buffer accesses, hence a raw buffer store over a wave-uniform base; being
+// compiler-visible, it also gets the wait states that a store of more than
+// 8 bytes needs before its data registers may be rewritten.
+constexpr int kCpolSc1Nt = 16 | 2;                   // cache-policy operand: sc1 = 16, nt = 2
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, int bytes) {
+    // base is the same in every lane of the wave; reading it from the first
+    // lane lets the compiler keep the descriptor in scalar registers (else it
+    // may wrap each store in a loop over distinct descriptors)
+    const uint64_t a = reinterpret_cast<uintptr_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    // raw (stride 0) descriptor over [base, base + bytes), 32-bit data format
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(hi << 32 | lo), 0, bytes, 0x00020000);
+}
+
 // One lane's share of a state row: VEC consecutive elements, 16 (or 8) bytes.
 template <typename TS, int VEC> struct Chunk;
 
@@ -142,6 +163,11 @@ template <> struct Chunk<float, 4> {
     static __device__ __forceinline__ void store(float* p, const float* f) {
         f32x4 r = {f[0], f[1], f[2], f[3]};
         __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+    }
+    // at byte offset off of a stream_rsrc buffer, agent scope + non-temporal
+    static __device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t rs, int off, const float* f) {
+        const u32x4 r = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(r, rs, off, 0, kCpolSc1Nt);
     }
 };
 
@@ -158,6 +184,11 @@ template <> struct Chunk<uint16_t, 8> {
         u32x4 r = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
                    pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
         __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+    }
+    static __device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t rs, int off, const float* f) {
+        const u32x4 r = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                         pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(r, rs, off, 0, kCpolSc1Nt);
     }
 };
 

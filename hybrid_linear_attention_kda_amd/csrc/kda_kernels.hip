@@ -47,6 +47,7 @@ namespace kda {
 // FUSED   true: conv prologue from bf16 x + conv state; false: f32 q|k|v input
 // XG      keep the NSPLIT workgroups of a head on one XCD (they read the same
 //         q/k inputs, which then come from that XCD's L2)
+// WT      state stores with agent scope as well as non-temporal (store_sc1)
 template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP>
 struct Geo {
     static constexpr int NT = NWAVES * 64;
@@ -260,7 +261,7 @@ __device__ __forceinline__ void conv_unit(const Pro& in, const Ptrs& p, int unit
 // The rest of one unit, after conv_unit and a barrier: norms, fade and both
 // reductions, one cross-wave exchange, delta correction, readout, rank-1
 // write and the stores.
-template <typename TS, class G, int D, int MODE>
+template <typename TS, class G, int D, int MODE, bool WT>
 __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&raw)[G::RPL], const Ptrs& p,
                                             int unit, int split, Smem<G, D>& sm) {
     constexpr int NT = G::NT, COLS = G::COLS, CG = G::CG, RPL = G::RPL, VEC = G::IO_VEC;
@@ -364,11 +365,16 @@ __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&r
 
     // ---- rank-1 write and store ----
     TS* const st = static_cast<TS*>(p.state) + (size_t)unit * D * D;
+    const auto rs = stream_rsrc(st, D * D * (int)sizeof(TS));   // used with WT only
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) sreg[t][e] = fmaf(kk[t], d[e], sreg[t][e]);
-        G::IO::store(st + (size_t)G::row(wv, rw, t) * D + col0, sreg[t]);
+        const int off = G::row(wv, rw, t) * D + col0;
+        if constexpr (WT)
+            G::IO::store_sc1(rs, off * (int)sizeof(TS), sreg[t]);
+        else
+            G::IO::store(st + off, sreg[t]);
     }
 
     // ---- gated RMSNorm of the head's outputs (MODE 2), "GLM-5.3 deep dive"
@@ -408,7 +414,7 @@ __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&r
 // One workgroup per (unit, split): grid M*H*NSPLIT.  The small prologue
 // loads go first, then every state load of the lane (all in flight
 // together); the conv + SiLU runs while the state is still arriving.
-template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG, int MODE>
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG, int MODE, bool WT>
 __global__ __launch_bounds__(NWAVES * 64)
 void decode_kernel(const Ptrs p, const int units)
 {
@@ -426,7 +432,7 @@ void decode_kernel(const Ptrs p, const int units)
     __builtin_amdgcn_sched_barrier(0);
     conv_unit<G, D, FUSED, MODE>(in, p, unit, split, sm);
     lds_barrier();
-    update_unit<TS, G, D, MODE>(in, raw, p, unit, split, sm);
+    update_unit<TS, G, D, MODE, WT>(in, raw, p, unit, split, sm);
 }
 
 // ------------------------------------------------------- T tokens per launch --
@@ -733,7 +739,8 @@ void conv_kernel(const int M, const int C, const uint16_t* __restrict__ x,
 // ---------------------------------------------------------------- launch --
 
 
-template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, bool FUSED, bool XG, int RMAP = 0, int MODE = 0>
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, bool FUSED, bool XG, int RMAP = 0, int MODE = 0,
+          bool WT = false>
 static hipError_t launch_decode(const StepArgs& a) {
     Ptrs p = make_ptrs(a);
     int units = a.M * a.H;
@@ -741,7 +748,7 @@ static hipError_t launch_decode(const StepArgs& a) {
     const dim3 grid((unsigned)((long)units * NSPLIT));
     const dim3 block(NWAVES * 64);
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&decode_kernel<TS, D, NSPLIT, NWAVES, VEC, RMAP, FUSED, XG, MODE>), grid,
+        reinterpret_cast<const void*>(&decode_kernel<TS, D, NSPLIT, NWAVES, VEC, RMAP, FUSED, XG, MODE, WT>), grid,
         block, args, 0, (hipStream_t)a.stream);
 }
 
@@ -751,6 +758,10 @@ static hipError_t launch_decode(const StepArgs& a) {
 //    waves (4 rows per lane) once there are >= 2048 heads to run.
 //  bf16, whole head per workgroup: 8 waves, each owning a band of 16 rows.
 //  column splits (small M*H only): 8 waves (f32, 2-way), else 4 waves.
+//  state stores with agent scope (WT) once there are >= 2048 heads, i.e.
+//    several rounds of workgroups per CU: 1.5% faster at 32 x 64 heads (f32)
+//    and 0.8% at 128 x 64 (bf16); 15% slower at 1 x 64, where one round of
+//    workgroups waits for its own last stores.
 // A split leaves every workgroup a row segment of >= 128 bytes for f32 at
 // 2- and 4-way and bf16 at 2-way; bf16 at 4-way (64 bytes) is supported but
 // shares cache lines between workgroups and is never chosen by the library.
@@ -758,7 +769,7 @@ static hipError_t launch_decode(const StepArgs& a) {
 template <bool FUSED, int MODE>
 static hipError_t dispatch_wide_f32(const StepArgs& a) {
     if (a.nsplit == 1)
-        return (long)a.M * a.H >= 2048 ? launch_decode<float, 128, 1, 16, 4, FUSED, false, 0, MODE>(a)
+        return (long)a.M * a.H >= 2048 ? launch_decode<float, 128, 1, 16, 4, FUSED, false, 0, MODE, true>(a)
                                        : launch_decode<float, 128, 1, 8, 4, FUSED, false, 0, MODE>(a);
     if constexpr (MODE != 2) {
         if (a.nsplit == 2) return launch_decode<float, 128, 2, 8, 4, FUSED, true, 0, MODE>(a);
@@ -769,7 +780,9 @@ static hipError_t dispatch_wide_f32(const StepArgs& a) {
 
 template <bool FUSED, int MODE>
 static hipError_t dispatch_wide_bf16(const StepArgs& a) {
-    if (a.nsplit == 1) return launch_decode<uint16_t, 128, 1, 8, 8, FUSED, false, 1, MODE>(a);
+    if (a.nsplit == 1)
+        return (long)a.M * a.H >= 2048 ? launch_decode<uint16_t, 128, 1, 8, 8, FUSED, false, 1, MODE, true>(a)
+                                       : launch_decode<uint16_t, 128, 1, 8, 8, FUSED, false, 1, MODE>(a);
     if constexpr (MODE != 2) {
         if (a.nsplit == 2) return launch_decode<uint16_t, 128, 2, 4, 8, FUSED, true, 0, MODE>(a);
         if (a.nsplit == 4) return launch_decode<uint16_t, 128, 4, 4, 8, FUSED, true, 0, MODE>(a);

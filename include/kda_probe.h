@@ -20,12 +20,13 @@ extern "C" {
 #endif
 
 /* In place: buf[i] = buf[i] * scale over `bytes` bytes of f32, each 16-byte
- * chunk read once and written once with non-temporal accesses (the state
- * update's read-once/write-once contract).  HBM traffic: 2 * bytes. */
+ * chunk read once and written once (the state update's read-once/write-once
+ * contract): non-temporal loads, non-temporal agent-scope stores, as the
+ * decode kernel's state accesses on large grids.  HBM traffic: 2 * bytes. */
 int kda_probe_rmw(void *buf, size_t bytes, float scale, void *stream);
 
-/* dst = src over `bytes` bytes, 16-byte non-temporal accesses; the buffers
- * must not overlap.  HBM traffic: 2 * bytes. */
+/* dst = src over `bytes` bytes, 16-byte accesses with the same cache policy
+ * as kda_probe_rmw; the buffers must not overlap.  HBM traffic: 2 * bytes. */
 int kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 #ifdef __cplusplus

@@ -122,6 +122,21 @@ def test_gated_split_path(orc, state_dtype):
     say(f"gated split {state_dtype}: out {e[0]:.3e} state {e[1]:.3e}")
 
 
+@pytest.mark.parametrize("layer_step", [False, True], ids=["gated", "layer"])
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+def test_gated_wide_grid(orc, state_dtype, layer_step):
+    """33 x 64 = 2112 heads, whole tensors: the launches that store the state
+    with agent scope (from 2048 heads on), with a partial last round of
+    workgroups."""
+    wl = kda_synth.custom("gated_wide", 33, 64, 128, steps=2)
+    lay = GatedLayer(wl, 0, state_dtype)
+    S_ref, cs_ref = host(lay.state), host(lay.conv)
+    for t in range(wl.steps):
+        S_ref, cs_ref, e = check_step(orc, lay, S_ref, cs_ref, t, KDA_GATE_BOUNDED, -5.0, layer_step,
+                                      teacher=state_dtype == "bf16")
+    say(f"{'layer' if layer_step else 'gated'} wide {state_dtype}: out {e[0]:.3e} state {e[1]:.3e}")
+
+
 def test_layer_step_glm_m32_sampled(orc):
     """Full geometry, M = 32 (the launch shape the benchmark times): the
     whole layer against the oracle on sampled (stream, head) units."""

@@ -230,6 +230,22 @@ def test_many_units_ragged(orc, state_dtype, inplace):
     say(f"many units {state_dtype} inplace={inplace}: o {e[0]:.3e} state {e[1]:.3e}")
 
 
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+def test_wide_grid_whole_tensors(orc, state_dtype):
+    """33 x 64 = 2112 heads, whole tensors: from 2048 heads on, the whole-head
+    launches store the state through agent-scope buffer stores instead of
+    global stores, and 2112 is not a multiple of the CU count, so the last
+    round of workgroups is partial."""
+    wl = kda_synth.custom("wide", 33, 64, 128, steps=2)
+    lay = Layer(wl, 0, DEV, state_dtype)
+    S_ref, cs_ref = host(lay.state), host(lay.conv)
+    for t in range(wl.steps):
+        S_ref, cs_ref, e = full_step_check(orc, lay, S_ref, cs_ref,
+                                           kda_synth.step_inputs(wl, 0, t, DEV), tol_state(state_dtype),
+                                           teacher=state_dtype == "bf16")
+    say(f"wide grid {state_dtype}: o {e[0]:.3e} state {e[1]:.3e}")
+
+
 def test_empty_batch():
     from hybrid_linear_attention_kda_amd import kda_decode_step
     e = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device=DEV)  # noqa: E731

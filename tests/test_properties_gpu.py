@@ -127,8 +127,9 @@ def test_conv_step_against_oracle(orc):
 
 
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("M", [4, 25])
+@pytest.mark.parametrize("M", [4, 25, 33])
 def test_recurrent_step_against_oracle(orc, state_dtype, M):
+    """M = 33: 2112 heads, the launch that stores the state with agent scope."""
     H, D = 64, 128
     wl = kda_synth.custom("rec", M, H, D)
     S = kda_synth.initial_state(wl, 0, DEV, state_dtype)
