@@ -254,50 +254,62 @@ void prefill_kernel(const Ptrs p, const int L)
                 S[mt][nt][r] = load_state_elem(st + (size_t)(16 * mt + 4 * g4 + r) * PD + ncol + 16 * nt + l16);
 
     // ---- per-lane constants of the input phase ----
-    // waves 0..2: channels 2 lane, 2 lane + 1 of q, k or v (tensor wv)
-    const size_t ch = (size_t)(wv < 3 ? wv : 0) * HD + (size_t)h * PD + 2 * lane;
+    // waves 0, 1: channels 2 lane, 2 lane + 1 of q (wave 0) or k (wave 1);
+    // waves 2, 3: channel vc = 64 (wave - 2) + lane of v and of the forget
+    // gate, so that the gate's transcendentals (four per element against
+    // two for a conv output) are shared by two waves rather than loading the
+    // fourth SIMD alone.  Wave 3's lanes 0..15 also take the write strength.
+    const bool qk = wv < 2;
+    const int vc = 64 * (wv & 1) + lane;
+    const size_t ch = qk ? (size_t)wv * HD + (size_t)h * PD + 2 * lane : 2 * HD + (size_t)h * PD + vc;
+    const size_t fc = (size_t)h * PD + vc;              // gate channel (waves 2, 3)
     float cw[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f;                // raw inputs of the 3 previous tokens, channel 2 lane
-    float b0 = 0.f, b1 = 0.f, b2 = 0.f;                // the same, channel 2 lane + 1
-    // wave 3: forget gate of channels 2 lane, 2 lane + 1
-    float db0 = 0.f, db1 = 0.f;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f;                // raw inputs of the 3 previous tokens, channel 2 lane (or vc)
+    float b0 = 0.f, b1 = 0.f, b2 = 0.f;                // the same, channel 2 lane + 1 (waves 0, 1)
     const float eA = expf(p.A_log[h]);
     const float lb = p.lower_bound;
-    if (wv < 3) {
+    const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
+    float db = 0.f;
+    if (qk) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
         cw[0] = bf16_lo(w.x); cw[1] = bf16_hi(w.x); cw[2] = bf16_lo(w.y); cw[3] = bf16_hi(w.y);
         cw[4] = bf16_lo(w.z); cw[5] = bf16_hi(w.z); cw[6] = bf16_lo(w.w); cw[7] = bf16_hi(w.w);
-        const uint16_t* ci = p.conv_in + (size_t)m * 3 * C3 + ch;
         const uint32_t t0v = *reinterpret_cast<const uint32_t*>(ci);
         const uint32_t t1v = *reinterpret_cast<const uint32_t*>(ci + C3);
         const uint32_t t2v = *reinterpret_cast<const uint32_t*>(ci + 2 * C3);
         a0 = bf16_lo(t0v); a1 = bf16_lo(t1v); a2 = bf16_lo(t2v);
         b0 = bf16_hi(t0v); b1 = bf16_hi(t1v); b2 = bf16_hi(t2v);
     } else {
-        db0 = p.dt_bias[(size_t)h * PD + 2 * lane];
-        db1 = p.dt_bias[(size_t)h * PD + 2 * lane + 1];
+        const u32x2 w = *reinterpret_cast<const u32x2*>(p.conv_w + 4 * ch);
+        cw[0] = bf16_lo(w.x); cw[1] = bf16_hi(w.x); cw[2] = bf16_lo(w.y); cw[3] = bf16_hi(w.y);
+        a0 = bf16_lo(ci[0]); a1 = bf16_lo(ci[C3]); a2 = bf16_lo(ci[2 * C3]);
+        db = p.dt_bias[fc];
     }
 
-    // raw inputs of one chunk: waves 0..2 x (2 bf16 per token), wave 3 the
-    // forget-gate projection (2 bf16 per token) and, lanes 0..15, the
-    // write-strength logit of token `lane`.  Past the end of the sequence
-    // the last token is read again; its results are masked out.
-    uint32_t raw[PC];
-    uint32_t rawb = 0;
+    // raw inputs of one chunk, two 16-bit streams per lane: waves 0, 1 the
+    // bf16 of channels 2 lane (raw) and 2 lane + 1 (rawf) of q or k; waves
+    // 2, 3 the bf16 of v (raw) and of the forget-gate projection (rawf); and
+    // in every wave the write-strength logit of token lane % 16 (used by
+    // wave 3).  Every wave issues the same loads from pointers chosen by its
+    // role, so the loaded registers are the loop-carried ones: loads written
+    // per role make the compiler copy the registers where the role paths
+    // join, which waits for the loads right after issuing them.  Past the
+    // end of the sequence the last token is read again; its results are
+    // masked out.
+    const uint16_t* const s1 = p.x + (size_t)m * L * C3 + ch;
+    const uint16_t* const s2 = qk ? s1 + 1 : p.fgate + (size_t)m * L * HD + fc;
+    const size_t d2 = qk ? C3 : HD;                     // token stride of s2
+    const uint16_t* const sb = p.blogit + (size_t)m * L * p.H + h;
+    uint32_t raw[PC], rawf[PC], rawb;
     auto fetch = [&](int t0) {
         const int last = min(PC, L - t0) - 1;
-        if (wv < 3) {
-            const uint16_t* xp = p.x + ((size_t)m * L + t0) * C3 + ch;
 #pragma unroll
-            for (int j = 0; j < PC; ++j)
-                raw[j] = *reinterpret_cast<const uint32_t*>(xp + (size_t)min(j, last) * C3);
-        } else {
-            const uint16_t* fp = p.fgate + ((size_t)m * L + t0) * HD + (size_t)h * PD + 2 * lane;
-#pragma unroll
-            for (int j = 0; j < PC; ++j)
-                raw[j] = *reinterpret_cast<const uint32_t*>(fp + (size_t)min(j, last) * HD);
-            rawb = p.blogit[((size_t)m * L + t0 + min(lane & (PC - 1), last)) * p.H + h];
+        for (int j = 0; j < PC; ++j) {
+            const size_t t = (size_t)(t0 + min(j, last));
+            raw[j] = s1[t * C3];
+            rawf[j] = s2[t * d2];
         }
+        rawb = sb[(size_t)(t0 + min(lane & (PC - 1), last)) * p.H];
     };
     fetch(0);
 
@@ -305,13 +317,13 @@ void prefill_kernel(const Ptrs p, const int L)
         const int n = min(PC, L - t0);
 
         // ---- 1. inputs ----
-        if (wv < 3) {
+        if (qk) {
             // tokens past the end give 0 (the carried taps are then stale,
             // but only the last chunk has such tokens)
             float z0[PC], z1[PC];
 #pragma unroll
             for (int j = 0; j < PC; ++j) {
-                const float x0 = bf16_lo(raw[j]), x1 = bf16_hi(raw[j]);
+                const float x0 = bf16_lo(raw[j]), x1 = bf16_lo(rawf[j]);
                 float y0 = cw[0] * a0;
                 y0 = fmaf(cw[1], a1, y0);
                 y0 = fmaf(cw[2], a2, y0);
@@ -326,44 +338,42 @@ void prefill_kernel(const Ptrs p, const int L)
                 a0 = a1; a1 = a2; a2 = x0;
                 b0 = b1; b1 = b2; b2 = x1;
             }
-            if (t0 + PC < L) fetch(t0 + PC);
-            float (*dst)[LS] = wv == 0 ? sm.qi[0] : wv == 1 ? sm.kh : sm.vv;
-            if (wv < 2) {
-                float ss[PC];
+            float (*dst)[LS] = wv == 0 ? sm.qi[0] : sm.kh;
+            float ss[PC];
 #pragma unroll
-                for (int j = 0; j < PC; ++j) ss[j] = fmaf(z0[j], z0[j], z1[j] * z1[j]);
-                const float tot = wave_sum16(ss, lane);
-                const float rn = (wv == 0 ? p.scale : 1.0f) * rsqrtf(tot + 1e-6f);
-#pragma unroll
-                for (int j = 0; j < PC; ++j) {
-                    const float rj = lane_value(rn, sum16_lane(j));
-                    z0[j] *= rj;
-                    z1[j] *= rj;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < PC; ++j)
-                *reinterpret_cast<float2*>(&dst[j][2 * lane]) = make_float2(z0[j], z1[j]);
-        } else {
-            // g = lb * sigmoid(exp(A) (f + b)), alpha = e^g; Gamma_j is the
-            // running product of alpha from the chunk start (the decay the
-            // per-token recurrence applies between the chunk start and j)
-            float e0 = 1.f, e1 = 1.f;
+            for (int j = 0; j < PC; ++j) ss[j] = fmaf(z0[j], z0[j], z1[j] * z1[j]);
+            const float tot = wave_sum16(ss, lane);
+            const float rn = (wv == 0 ? p.scale : 1.0f) * rsqrtf(tot + 1e-6f);
 #pragma unroll
             for (int j = 0; j < PC; ++j) {
-                const float g0 = lb * __builtin_amdgcn_rcpf(1.0f + exp_fast(-eA * (bf16_lo(raw[j]) + db0)));
-                const float g1 = lb * __builtin_amdgcn_rcpf(1.0f + exp_fast(-eA * (bf16_hi(raw[j]) + db1)));
-                e0 *= j < n ? exp_fast(g0) : 1.f;
-                e1 *= j < n ? exp_fast(g1) : 1.f;
-                *reinterpret_cast<float2*>(&sm.eg[j][2 * lane]) = make_float2(e0, e1);
-                *reinterpret_cast<float2*>(&sm.qi[1][j][2 * lane]) =
-                    make_float2(__builtin_amdgcn_rcpf(e0), __builtin_amdgcn_rcpf(e1));
+                const float rj = lane_value(rn, sum16_lane(j));
+                *reinterpret_cast<float2*>(&dst[j][2 * lane]) = make_float2(z0[j] * rj, z1[j] * rj);
             }
-            *reinterpret_cast<float2*>(&sm.gam[2 * lane]) = make_float2(e0, e1);
-            if (lane < PC)
+        } else {
+            // v: conv + SiLU as above.  Gate: g = lb * sigmoid(exp(A) (f + b)),
+            // alpha = e^g; Gamma_j is the running product of alpha from the
+            // chunk start (the decay the per-token recurrence applies between
+            // the chunk start and j)
+            float e = 1.f;
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+                const float x0 = bf16_lo(raw[j]);
+                float y0 = cw[0] * a0;
+                y0 = fmaf(cw[1], a1, y0);
+                y0 = fmaf(cw[2], a2, y0);
+                y0 = fmaf(cw[3], x0, y0);
+                sm.vv[j][vc] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
+                a0 = a1; a1 = a2; a2 = x0;
+                const float g = lb * __builtin_amdgcn_rcpf(1.0f + exp_fast(-eA * (bf16_lo(rawf[j]) + db)));
+                e *= j < n ? exp_fast(g) : 1.f;
+                sm.eg[j][vc] = e;
+                sm.qi[1][j][vc] = __builtin_amdgcn_rcpf(e);
+            }
+            sm.gam[vc] = e;
+            if (wv == 3 && lane < PC)
                 sm.beta[lane] = lane < n ? __builtin_amdgcn_rcpf(1.0f + exp_fast(-bf16_lo(rawb))) : 0.0f;
-            if (t0 + PC < L) fetch(t0 + PC);
         }
+        if (t0 + PC < L) fetch(t0 + PC);
         lds_barrier();
 
         // ---- 2. A (waves 0, 1) and P (waves 2, 3), each wave one half of the
@@ -569,17 +579,28 @@ void prefill_kernel(const Ptrs p, const int L)
     // overwrites it: conv_out may be conv_in, and each lane owns its channels;
     // with NS = 2 the first workgroup of the head writes it, and the host
     // requires conv_out != conv_in, since the other one reads conv_in)
-    if (wv < 3 && split == 0) {
-        uint32_t nt3[3];
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int pos = L - 3 + k;
-            nt3[k] = pos < 0 ? *reinterpret_cast<const uint32_t*>(p.conv_in + (size_t)m * 3 * C3 + (size_t)(3 + pos) * C3 + ch)
-                             : *reinterpret_cast<const uint32_t*>(p.x + ((size_t)m * L + pos) * C3 + ch);
-        }
+    if (split == 0) {
         uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + ch;
+        if (qk) {
+            uint32_t nt3[3];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) *reinterpret_cast<uint32_t*>(co + (size_t)k * C3) = nt3[k];
+            for (int k = 0; k < 3; ++k) {
+                const int pos = L - 3 + k;
+                nt3[k] = pos < 0 ? *reinterpret_cast<const uint32_t*>(ci + (size_t)(3 + pos) * C3)
+                                 : *reinterpret_cast<const uint32_t*>(p.x + ((size_t)m * L + pos) * C3 + ch);
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) *reinterpret_cast<uint32_t*>(co + (size_t)k * C3) = nt3[k];
+        } else {
+            uint16_t nt3[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int pos = L - 3 + k;
+                nt3[k] = pos < 0 ? ci[(size_t)(3 + pos) * C3] : p.x[((size_t)m * L + pos) * C3 + ch];
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) co[(size_t)k * C3] = nt3[k];
+        }
     }
 }
 
