@@ -81,7 +81,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // round-to-nearest-even bf16 of what the previous ones leave (the remainder
 // is exact in f32).  A product of two split operands then takes the six
 // terms x_a y_b with a + b <= 4 (pieces numbered from 1), which keeps
-// products to f32 accuracy while running on the bf16 matrix cores.
+// products to f32 accuracy while running on the bf16 matrix cores.  The one
+// product that feeds only the output, (Gamma . Q) S, takes the three terms
+// with a + b <= 3: each dropped term is below 2^-17 of its product (RNE
+// pieces: |x - x1| <= 2^-9 |x|, |x - x1 - x2| <= 2^-18 |x|), far inside the
+// output's single bf16 rounding, while the state keeps f32 accuracy.
 // Fragments hold 8 bf16 (one per k slot of v_mfma_f32_16x16x32_bf16), as
 // 4 dwords, slot 2i in the low half of dword i.
 struct PrefillSmem {
@@ -92,7 +96,7 @@ struct PrefillSmem {
         float qi[2][PC][LS];       // [0] q^ (normalised, scaled), [1] 1 / Gamma; dead after phase 2
         u32x4 dp[3][4][2][2][16];  // Delta pieces [piece][wave][tile][token half][column]: 8 tokens each
     };
-    u32x4 gqp[3][4][64];           // (Gamma . q^) pieces [piece][32-row block][lane]: A operand of the state products
+    u32x4 gqp[2][4][64];           // (Gamma . q^) pieces 1, 2 [piece][32-row block][lane]: A operand of (Gamma . Q) S
     u32x4 ktp[3][8][2][16];        // ((gamma_C / Gamma) . k^) pieces [piece][row tile][token half][row]
     float Z[2][PC][LT];            // Z[j][i] = sum_c (Gamma . k^)[i][c] (k^ / Gamma)[j][c], per channel half
     float P[2][PC][LT];            // Tril((Gamma . q^)(k^ / Gamma)^T), row = query token, per channel half
@@ -420,7 +424,7 @@ void prefill_kernel(const Ptrs p, const int L)
                 split8(lds4(&sm.qi[0][tk][c0]) * lds4(&sm.eg[tk][c0]),
                        lds4(&sm.qi[0][tk][c0 + 16]) * lds4(&sm.eg[tk][c0 + 16]), pc);
 #pragma unroll
-                for (int q = 0; q < 3; ++q) sm.gqp[q][kb][ln] = pc[q];
+                for (int q = 0; q < 2; ++q) sm.gqp[q][kb][ln] = pc[q];
             }
             // (gamma_C / Gamma) . k^: fragment (row tile mt, token half hf, row)
             // holds 8 tokens of state row 16 mt + row
@@ -464,7 +468,8 @@ void prefill_kernel(const Ptrs p, const int L)
         // column tile (rows 32 kb + 4 (lane / 16) + {0..3, 16..19}: its own
         // registers) are the B fragment; the A fragments (-W and Gamma . q^
         // of token lane % 16 at the same rows) come split from LDS.  Six bf16
-        // products per pair of split operands.
+        // products per pair of split operands for W S (the state's path),
+        // the first three of them for (Gamma . Q) S (the output's).
         f32x4 dacc[NTW], oacc[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
@@ -474,7 +479,7 @@ void prefill_kernel(const Ptrs p, const int L)
         }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            u32x4 sb[NTW][3], wp[3], gp[3];
+            u32x4 sb[NTW][3], wp[3], gp[2];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
                 split8(f32x4{S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3]},
@@ -482,13 +487,13 @@ void prefill_kernel(const Ptrs p, const int L)
                        sb[nt]);
             split8(lds4(&sm.kh[l16][32 * kb + 4 * g4]), lds4(&sm.kh[l16][32 * kb + 16 + 4 * g4]), wp);   // -W
 #pragma unroll
-            for (int q = 0; q < 3; ++q) gp[q] = sm.gqp[q][kb][lane];
+            for (int q = 0; q < 2; ++q) gp[q] = sm.gqp[q][kb][lane];
 #pragma unroll
             for (int pr = 0; pr < 6; ++pr)
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     dacc[nt] = mfma_bf16(wp[PAIR_A[pr]], sb[nt][PAIR_B[pr]], dacc[nt]);
-                    oacc[nt] = mfma_bf16(gp[PAIR_A[pr]], sb[nt][PAIR_B[pr]], oacc[nt]);
+                    if (pr < 3) oacc[nt] = mfma_bf16(gp[PAIR_A[pr]], sb[nt][PAIR_B[pr]], oacc[nt]);
                 }
         }
         // Delta replaces Gamma, which nobody reads any more; its pieces go
