@@ -67,6 +67,43 @@ def test_split_agrees_to_rounding(orc, state_dtype):
         assert rel_err(host(lay.state), S_ref) <= (1e-5 if state_dtype == "f32" else 4e-3)
 
 
+@pytest.mark.parametrize("entry", ["plain", "gated", "layer"])
+def test_store_policy_bitwise_bf16(entry):
+    """bf16 state: the same whole-head kernel runs below and above 2048 heads;
+    only the state store's cache policy differs (agent scope from 2048 heads
+    on).  32 streams (2048 heads) and their first 31 (1984 heads) in a call of
+    their own must agree bit for bit on those 31 streams."""
+    from hybrid_linear_attention_kda_amd import (KDA_GATE_BOUNDED, kda_decode_layer_step,
+                                                 kda_decode_step_gated)
+    M, H, D = 32, 64, 128
+    wl = kda_synth.custom("policy", M, H, D, steps=1)
+    li = kda_synth.layer_inputs(wl, 0, DEV, "bf16")
+    inp = kda_synth.step_inputs(wl, 0, 0, DEV)
+    gp = kda_synth.gate_params(wl, 0, DEV)
+    gi = kda_synth.gate_inputs(wl, 0, 0, DEV)
+    outs = []
+    for m in (M, M - 1):
+        S = li["state"][:m].clone()
+        cs = li["conv_state"][:m].clone()
+        o = torch.empty((m, H, D), dtype=torch.bfloat16, device=DEV)
+        if entry == "plain":
+            kda_decode_step(S, inp["x"][:m], li["conv_w"], cs, cs, inp["alpha"][:m], inp["beta"][:m],
+                            wl.scale, o)
+        elif entry == "gated":
+            kda_decode_step_gated(S, inp["x"][:m], li["conv_w"], cs, cs, gi["f"][:m], gp["A_log"],
+                                  gp["dt_bias"], gi["beta_logit"][:m], wl.scale, o,
+                                  gate_kind=KDA_GATE_BOUNDED, lower_bound=-5.0)
+        else:
+            kda_decode_layer_step(S, inp["x"][:m], li["conv_w"], cs, cs, gi["f"][:m], gp["A_log"],
+                                  gp["dt_bias"], gi["beta_logit"][:m], wl.scale, gi["out_gate"][:m],
+                                  gp["norm_w"], o, gate_kind=KDA_GATE_BOUNDED, lower_bound=-5.0)
+        outs.append((S, cs, o))
+    torch.cuda.synchronize()
+    (S1, c1, o1), (S2, c2, o2) = outs
+    n = M - 1
+    assert torch.equal(S1[:n], S2) and torch.equal(c1[:n], c2) and torch.equal(o1[:n], o2)
+
+
 def test_inplace_conv_equals_pingpong():
     wl = kda_synth.custom("pp", 3, 8, 128, steps=4)
     a, oa = run(wl, "f32", 4, nsplit=1, inplace=True)
