@@ -491,52 +491,58 @@ __device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, 
     const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
     // ALL: every item's loads go out before any is used (the chunk waits
     // for memory once); otherwise item by item, which holds a third of the
-    // registers (chunks after the first, when the state is in registers)
-    u32x2 xv[IT], t0[IT], t1[IT], t2[IT];
-    u32x4 w01[IT], w23[IT];
-    f32x4 av[IT];
-    float bv[IT];
-    auto load_item = [&](int k) {
+    // registers (chunks after the first, when the state is in registers).
+    // An item's inputs live in a struct of its own, so the item-by-item loop
+    // (not unrolled) indexes no register array at a run-time position.
+    struct Item {
+        u32x2 xv, t0, t1, t2;
+        u32x4 w01, w23;
+        f32x4 av;
+        float bv;
+    };
+    auto load_item = [&](int k, Item& it) {
         const int idx = tid + k * G::NT, j = idx / MG::NGT, g = idx - j * MG::NGT;
         if (j < n) {
             const int tok = c0 + j;
             const size_t ch = group_channel<G, D>(g, h, 0, HD);
-            xv[k] = seq_input(p, T, m, C3, ch, tok);
-            t2[k] = seq_input(p, T, m, C3, ch, tok - 1);
-            t1[k] = seq_input(p, T, m, C3, ch, tok - 2);
-            t0[k] = seq_input(p, T, m, C3, ch, tok - 3);
+            it.xv = seq_input(p, T, m, C3, ch, tok);
+            it.t2 = seq_input(p, T, m, C3, ch, tok - 1);
+            it.t1 = seq_input(p, T, m, C3, ch, tok - 2);
+            it.t0 = seq_input(p, T, m, C3, ch, tok - 3);
             const u32x4* wp = reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
-            w01[k] = wp[0];
-            w23[k] = wp[1];
+            it.w01 = wp[0];
+            it.w23 = wp[1];
             const size_t mt = (size_t)m * T + tok;
-            if (g < D / 4) av[k] = *reinterpret_cast<const f32x4*>(p.alpha + mt * HD + (size_t)h * D + 4 * g);
-            if (g == 0) bv[k] = p.beta[mt * p.H + h];
+            if (g < D / 4) it.av = *reinterpret_cast<const f32x4*>(p.alpha + mt * HD + (size_t)h * D + 4 * g);
+            if (g == 0) it.bv = p.beta[mt * p.H + h];
         }
     };
-    auto conv_item = [&](int k) {
+    auto conv_item = [&](int k, const Item& it) {
         const int idx = tid + k * G::NT, j = idx / MG::NGT, g = idx - j * MG::NGT;
         if (j < n) {
-            const u32x4 wa = w01[k], wb = w23[k];
-            const u32x2 x0 = t0[k], x1 = t1[k], x2 = t2[k], x3 = xv[k];
+            const u32x4 wa = it.w01, wb = it.w23;
+            const u32x2 x0 = it.t0, x1 = it.t1, x2 = it.t2, x3 = it.xv;
             reinterpret_cast<f32x4*>(sm.z[j])[g] =
                 f32x4{conv_silu(u32x2{wa.x, wa.y}, bf16_lo(x0.x), bf16_lo(x1.x), bf16_lo(x2.x), bf16_lo(x3.x)),
                       conv_silu(u32x2{wa.z, wa.w}, bf16_hi(x0.x), bf16_hi(x1.x), bf16_hi(x2.x), bf16_hi(x3.x)),
                       conv_silu(u32x2{wb.x, wb.y}, bf16_lo(x0.y), bf16_lo(x1.y), bf16_lo(x2.y), bf16_lo(x3.y)),
                       conv_silu(u32x2{wb.z, wb.w}, bf16_hi(x0.y), bf16_hi(x1.y), bf16_hi(x2.y), bf16_hi(x3.y))};
-            if (g < D / 4) reinterpret_cast<f32x4*>(sm.a[j])[g] = av[k];
-            if (g == 0) sm.b[j] = bv[k];
+            if (g < D / 4) reinterpret_cast<f32x4*>(sm.a[j])[g] = it.av;
+            if (g == 0) sm.b[j] = it.bv;
         }
     };
     if constexpr (ALL) {
+        Item its[IT];
 #pragma unroll
-        for (int k = 0; k < IT; ++k) load_item(k);
+        for (int k = 0; k < IT; ++k) load_item(k, its[k]);
 #pragma unroll
-        for (int k = 0; k < IT; ++k) conv_item(k);
+        for (int k = 0; k < IT; ++k) conv_item(k, its[k]);
     } else {
 #pragma unroll 1
         for (int k = 0; k < IT; ++k) {
-            load_item(k);
-            conv_item(k);
+            Item it;
+            load_item(k, it);
+            conv_item(k, it);
         }
     }
     lds_barrier();
@@ -645,7 +651,7 @@ __device__ __forceinline__ void multi_token(float (&sreg)[MG::G::RPL][MG::G::IO_
 // One workgroup per (stream, head), T >= 1 tokens; x [M][T][3][H*D],
 // alpha [M][T][H][D], beta [M][T][H], o [M][T][H][D].
 template <typename TS, int D, int NWAVES, int VEC, int RMAP, int TCMAX = 16>
-__global__ __launch_bounds__(NWAVES * 64, D == 128 ? 3 : 1)   // D = 128: 3 workgroups per CU
+__global__ __launch_bounds__(NWAVES * 64, D == 128 ? 4 : 1)   // D = 128: 4 workgroups per CU
 void decode_multi_kernel(const Ptrs p, const int units, const int T)
 {
     typedef MultiGeo<TS, D, NWAVES, VEC, RMAP, TCMAX> MG;
@@ -680,8 +686,15 @@ void decode_multi_kernel(const Ptrs p, const int units, const int T)
         lds_barrier();
     }
 
+    // the lane's state addresses, formed again here from a value the
+    // compiler cannot see into, so that they are not kept live (or spilled)
+    // across the token loop; both row maps place lane row rw at
+    // row(wv, 0, r) + rw
+    int lo = rw * D + cg * G::IO_VEC;
+    asm volatile("" : "+v"(lo));
+    TS* const so = static_cast<TS*>(p.state) + (size_t)unit * D * D + lo;
 #pragma unroll
-    for (int r = 0; r < G::RPL; ++r) G::IO::store(st + (size_t)G::row(wv, rw, r) * D, sreg[r]);
+    for (int r = 0; r < G::RPL; ++r) G::IO::store(so + (size_t)G::row(wv, 0, r) * D, sreg[r]);
     // conv state after T tokens: sequence positions T-3, T-2, T-1 (a
     // position < 0 is one of the cached taps, read before it is overwritten)
     if (tid < MG::NGT) {
