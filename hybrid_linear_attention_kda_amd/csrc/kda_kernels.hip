@@ -563,7 +563,7 @@ __device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, 
             const float rq = p.scale * rsqrtf(sqq + 1e-6f), rk = rsqrtf(skk + 1e-6f);
             sm.rq[t] = rq;
             sm.rk[t] = rk;
-            sm.kq[t] = sqk * rq * rk;
+            sm.kq[t] = sqk * rq;   // k^.q^ / rk: the token loop carries d rk
         }
     }
     lds_barrier();
@@ -581,14 +581,17 @@ __device__ __forceinline__ void multi_token(float (&sreg)[MG::G::RPL][MG::G::IO_
     const int cg = lane % CG, rw = lane / CG;
     const float rq = sm.rq[t], rk = sm.rk[t], kq = sm.kq[t], b = sm.b[t];
 
+    // the sums run over the conv outputs z_q, z_k themselves; the norms
+    // scale the column sums (u = rk S^T z_k, w = rq S^T z_q) and the update
+    // takes d rk against z_k, so no row is multiplied by rk or rq
     float kk[RPL], u[VEC], wq[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) { u[e] = 0.0f; wq[e] = 0.0f; }
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const int i = G::row(wv, rw, r);
-        const float a = sm.a[t][i], qq = sm.z[t][i] * rq;
-        kk[r] = sm.z[t][D + i] * rk;
+        const float a = sm.a[t][i], qq = sm.z[t][i];
+        kk[r] = sm.z[t][D + i];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const float sv = sreg[r][e] * a;
@@ -622,12 +625,12 @@ __device__ __forceinline__ void multi_token(float (&sreg)[MG::G::RPL][MG::G::IO_
             float U = 0.0f;
 #pragma unroll
             for (int w = 0; w < NWAVES; ++w) U += sm.red[w][0][tid];
-            sm.d[tid] = b * (sv_[tid] - U);
+            sm.d[tid] = rk * (b * (sv_[tid] - rk * U));
         } else if (tid < 2 * COLS) {
             float W = 0.0f;
 #pragma unroll
             for (int w = 0; w < NWAVES; ++w) W += sm.red[w][1][tid - COLS];
-            sm.w[tid - COLS] = W;
+            sm.w[tid - COLS] = rq * W;
         }
         lds_barrier();
 #pragma unroll
@@ -635,11 +638,11 @@ __device__ __forceinline__ void multi_token(float (&sreg)[MG::G::RPL][MG::G::IO_
         if (tid < COLS) ou[tid] = (uint16_t)f32_to_bf16_rne(fmaf(sm.d[tid], kq, sm.w[tid]));
     } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) d[e] = b * (sv_[cg * VEC + e] - u[e]);
+        for (int e = 0; e < VEC; ++e) d[e] = rk * (b * (sv_[cg * VEC + e] - rk * u[e]));
         if (rw == 0) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                ou[cg * VEC + e] = (uint16_t)f32_to_bf16_rne(fmaf(d[e], kq, wq[e]));
+                ou[cg * VEC + e] = (uint16_t)f32_to_bf16_rne(fmaf(d[e], kq, rq * wq[e]));
         }
     }
 #pragma unroll
