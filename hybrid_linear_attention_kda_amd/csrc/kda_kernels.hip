@@ -845,10 +845,13 @@ hipError_t launch_decode_multi(const StepArgs& a) {
     case 32: return f32 ? launch_multi<float, 32, 1, 4, 0, 2>(a) : launch_multi<uint16_t, 32, 1, 8, 0, 2>(a);
     case 64: return f32 ? launch_multi<float, 64, 2, 4, 0, 2>(a) : launch_multi<uint16_t, 64, 2, 8, 0, 2>(a);
     case 128:
-        // 4 waves per head (16 or 8 rows per lane), each wave a band of rows:
-        // the token loop is latency-bound, so more heads per CU beat more
-        // waves per head (measured)
-        return f32 ? launch_multi<float, 128, 4, 4, 1, 8>(a) : launch_multi<uint16_t, 128, 4, 8, 1, 8>(a);
+        // 4 waves per head, each wave a band of rows, 16 rows x 4 columns per
+        // lane for either state type (8-byte accesses for bf16: with 8
+        // columns per lane a row spans 16 lanes and every column sum takes
+        // two cross-lane steps instead of one); the token loop is
+        // latency-bound, so more heads per CU beat more waves per head
+        // (measured)
+        return f32 ? launch_multi<float, 128, 4, 4, 1, 8>(a) : launch_multi<uint16_t, 128, 4, 4, 1, 8>(a);
     default: return hipErrorInvalidValue;
     }
 }
