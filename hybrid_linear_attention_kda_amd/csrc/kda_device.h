@@ -204,6 +204,10 @@ template <> struct Chunk<uint16_t, 4> {
         u32x2 r = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
         __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(p));
     }
+    static __device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t rs, int off, const float* f) {
+        const u32x2 r = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(r, rs, off, 0, kCpolSc1Nt);
+    }
 };
 
 // e^x from the hardware 2^x (v_exp_f32) with the argument split into
