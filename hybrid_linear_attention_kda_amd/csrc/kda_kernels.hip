@@ -465,12 +465,14 @@ struct MultiGeo {
 
 template <class MG, int D>
 struct MultiSmem {
-    __attribute__((aligned(16))) float z[MG::TC][MG::ZW];
-    __attribute__((aligned(16))) float a[MG::TC][D];
-    float b[MG::TC], rq[MG::TC], rk[MG::TC], kq[MG::TC];
-    float red[MG::G::NT / 64][2][D];
-    float d[D];
-    float w[D];
+    __attribute__((aligned(16))) float z[MG::TC][MG::ZW];   // conv outputs q|k|v of the chunk's tokens
+    __attribute__((aligned(16))) float a[MG::TC][D];        // alpha
+    float b[MG::TC];                                         // beta
+    float rq[MG::TC], rk[MG::TC];                            // scale / |q|, 1 / |k| (the L2 norms)
+    float kq[MG::TC];                                        // k^.q^ / rk
+    float red[MG::G::NT / 64][2][D];                         // per-wave partial column sums (k, q)
+    float d[D];                                              // rk * delta of the current token
+    float w[D];                                              // S^T q^ of the current token
 };
 
 // Raw input (4 bf16 channels at channel offset ch) at sequence position pos
