@@ -773,7 +773,11 @@ static hipError_t launch_decode(const StepArgs& a) {
 // D = 128 launch shapes, from measurement on MI355X (34 layers of distinct
 // state, DRAM-resident):
 //  f32, whole head per workgroup: 8 waves (8 rows x 4 columns per lane); 16
-//    waves (4 rows per lane) once there are >= 2048 heads to run.
+//    waves (4 rows per lane) once there are >= 2048 heads to run.  With 8
+//    waves, each wave takes a band of rows (RMAP 1) when the grid is one
+//    round of workgroups over every CU (256 to 768 heads at 3 per CU: 4%
+//    faster at 512), interleaved rows otherwise (fewer heads: idle CUs;
+//    more: several rounds; both slower with bands).
 //  bf16, whole head per workgroup: 8 waves, each owning a band of 16 rows,
 //    8 rows x 4 columns per lane (8-byte accesses; with 8 columns per lane
 //    and 16-byte accesses a row spans 16 lanes and the column sums take two
@@ -789,9 +793,12 @@ static hipError_t launch_decode(const StepArgs& a) {
 // The output norm (MODE 2) needs a whole head per workgroup: no splits.
 template <bool FUSED, int MODE>
 static hipError_t dispatch_wide_f32(const StepArgs& a) {
-    if (a.nsplit == 1)
-        return (long)a.M * a.H >= 2048 ? launch_decode<float, 128, 1, 16, 4, FUSED, false, 0, MODE, true>(a)
-                                       : launch_decode<float, 128, 1, 8, 4, FUSED, false, 0, MODE>(a);
+    if (a.nsplit == 1) {
+        const long heads = (long)a.M * a.H;
+        if (heads >= 2048) return launch_decode<float, 128, 1, 16, 4, FUSED, false, 0, MODE, true>(a);
+        if (heads >= 256 && heads <= 768) return launch_decode<float, 128, 1, 8, 4, FUSED, false, 1, MODE>(a);
+        return launch_decode<float, 128, 1, 8, 4, FUSED, false, 0, MODE>(a);
+    }
     if constexpr (MODE != 2) {
         if (a.nsplit == 2) return launch_decode<float, 128, 2, 8, 4, FUSED, true, 0, MODE>(a);
         if (a.nsplit == 4) return launch_decode<float, 128, 4, 4, 4, FUSED, true, 0, MODE>(a);

@@ -94,7 +94,7 @@ KINDS = [(KDA_GATE_BOUNDED, -5.0), (KDA_GATE_SOFTPLUS, 0.0)]
 @pytest.mark.parametrize("layer_step", [False, True], ids=["gated", "layer"])
 @pytest.mark.parametrize("kind,lb", KINDS, ids=["bounded", "softplus"])
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("M,H,D", [(1, 4, 16), (2, 3, 32), (3, 2, 64), (3, 5, 128), (2, 64, 128)])
+@pytest.mark.parametrize("M,H,D", [(1, 4, 16), (2, 3, 32), (3, 2, 64), (3, 5, 128), (2, 64, 128), (8, 64, 128)])
 def test_gated_against_oracle(orc, M, H, D, state_dtype, kind, lb, layer_step):
     """Three consecutive steps; f32 state free-running, bf16 teacher-forced."""
     wl = kda_synth.custom(f"gated_{M}_{H}_{D}", M, H, D, steps=3)
