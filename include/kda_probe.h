@@ -4,11 +4,12 @@
  * contract and calibrate the profiler's byte counters.  Not part of the KDA
  * decode step.
  *
- * Both take DEVICE pointers the caller owns (16-byte aligned), enqueue one
+ * All take DEVICE pointers the caller owns (16-byte aligned), enqueue one
  * kernel on `stream` (a hipStream_t; NULL = default stream) and return
- * 0 = enqueued, 1 = NULL pointer, 4 = misaligned, 5 = src and dst overlap,
- * 6 = bytes is 0, not a multiple of 8192, or too large, 7 = launch refused.
- * Nothing is allocated, freed or synchronised.
+ * 0 = enqueued, 1 = NULL pointer, 4 = misaligned, 5 = src and dst overlap
+ * (or, in place, differ), 6 = bytes is 0, not a multiple of the tile, or too
+ * large, or an unknown shape, 7 = launch refused.  Nothing is allocated,
+ * freed or synchronised.
  */
 #ifndef KDA_PROBE_H
 #define KDA_PROBE_H
@@ -28,6 +29,21 @@ int kda_probe_rmw(void *buf, size_t bytes, float scale, void *stream);
 /* dst = src over `bytes` bytes, 16-byte accesses with the same cache policy
  * as kda_probe_rmw; the buffers must not overlap.  HBM traffic: 2 * bytes. */
 int kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* The ceiling sweep: one launch over `bytes` bytes in 16-byte chunks.
+ *   kind             0 in place (dst must equal src: read once, written once),
+ *                    1 read only (src; dst unused), 2 write only (dst is
+ *                    filled with `scale`; src unused), 3 copy (no overlap)
+ *   threads          256, 512 or 1024 per workgroup
+ *   chunks_per_lane  1, 2 or 4: a tile is threads * chunks_per_lane chunks;
+ *                    a lane issues all its loads before its first store
+ *   persistent       0: one workgroup per tile; 1: a grid of every wave slot
+ *                    of the device (32 waves per CU) walks the tiles
+ * bytes must be a multiple of the tile (threads * chunks_per_lane * 16).
+ * Same cache policy as kda_probe_rmw.  HBM traffic: 2 * bytes for kinds 0
+ * and 3, bytes for kinds 1 and 2.  In place multiplies by `scale`. */
+int kda_probe_stream(int kind, int threads, int chunks_per_lane, int persistent, const void *src, void *dst,
+                     size_t bytes, float scale, void *stream);
 
 #ifdef __cplusplus
 }

@@ -86,7 +86,7 @@ WORKLOADS = {
     "glm_m8": Workload("glm_m8", M=8, H=64, D=128, layers=34, steps=1, state_dtypes=("f32", "bf16"),
                        alpha_kind="u09", beta_kind="sigmoid", conv_init="normal", seed=2,
                        description="M=8 streams, 34 layers with distinct states, one step"),
-    "glm_m32": Workload("glm_m32", M=32, H=64, D=128, layers=34, steps=8, state_dtypes=("f32",),
+    "glm_m32": Workload("glm_m32", M=32, H=64, D=128, layers=34, steps=8, state_dtypes=("f32", "bf16"),
                         alpha_kind="u09", beta_kind="sigmoid", conv_init="normal", seed=3,
                         description="M=32 streams, 34 layers, FP32 state, 8 consecutive steps"),
     "glm_m128": Workload("glm_m128", M=128, H=64, D=128, layers=34, steps=8, state_dtypes=("bf16",),

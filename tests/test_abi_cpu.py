@@ -300,3 +300,15 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert plib.kda_probe_copy(fake(0), fake(0, 8), 8192, None) == 4
     assert plib.kda_probe_copy(fake(0), fake(0) + 4096, 8192, None) == 5
     assert plib.kda_probe_copy(fake(0), fake(1), 100, None) == 6
+    st = plib.kda_probe_stream
+    assert st(4, 512, 1, 0, fake(0), fake(0), 8192, 1.0, None) == 6          # unknown kind
+    assert st(0, 512, 1, 0, None, None, 8192, 1.0, None) == 1
+    assert st(1, 512, 1, 0, None, None, 8192, 1.0, None) == 1                 # read only needs src
+    assert st(2, 512, 1, 0, fake(0), None, 8192, 1.0, None) == 1              # write only needs dst
+    assert st(0, 512, 1, 0, fake(0, 8), fake(0, 8), 8192, 1.0, None) == 4
+    assert st(0, 512, 1, 0, fake(0), fake(1), 8192, 1.0, None) == 5           # in place: dst == src
+    assert st(3, 512, 1, 0, fake(0), fake(0) + 4096, 8192, 1.0, None) == 5    # copy: no overlap
+    assert st(0, 384, 1, 0, fake(0), fake(0), 8192, 1.0, None) == 6           # threads
+    assert st(0, 512, 3, 0, fake(0), fake(0), 8192, 1.0, None) == 6           # chunks per lane
+    assert st(0, 1024, 4, 0, fake(0), fake(0), 32768, 1.0, None) == 6         # not a whole tile
+    assert st(0, 512, 1, 0, fake(0), fake(0), 0, 1.0, None) == 6
