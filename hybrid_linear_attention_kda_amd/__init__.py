@@ -17,6 +17,7 @@ from .kda import (  # noqa: F401
     kda_decode_step,
     kda_decode_step_gated,
     kda_prefill_gated,
+    kda_prefill_workspace_bytes,
     kda_recurrent_step,
     kda_status_string,
     kda_version,

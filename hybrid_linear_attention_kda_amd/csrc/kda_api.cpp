@@ -51,11 +51,17 @@ int map_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 // buffers: the split workgroups of a head all read the head's q/k taps, so
 // none may overwrite them in place.  bf16 state splits at most 2-way (a
 // 4-way split would leave 64-byte row segments, half a cache line).
-int choose_split(int M, int H, int D, int sdt, bool conv_in_place) {
+// Compute units of the device the caller's stream runs on (256, MI355X's
+// count, if the runtime cannot tell).
+int stream_cus(void* stream) {
+    const int n = kda::stream_cu_count(stream);
+    return n > 0 ? n : 256;
+}
+
+int choose_split(int M, int H, int D, int sdt, bool conv_in_place, void* stream) {
     if (D != 128 || conv_in_place) return 1;
     const long units = (long)M * H;
-    int cus = kda::device_cu_count();
-    if (cus <= 0) cus = 256;
+    const int cus = stream_cus(stream);
     if (units >= cus) return 1;
     if (sdt == KDA_STATE_BF16 || 2 * units >= cus) return 2;
     return 4;
@@ -128,7 +134,7 @@ int run_decode(int M, int H, int D, int sdt, void* state, const void* x, const v
     if (rc != KDA_OK || M == 0) return rc;
     const bool in_place = cout == cin;
     if (nsplit == 0) {
-        nsplit = choose_split(M, H, D, sdt, in_place);
+        nsplit = choose_split(M, H, D, sdt, in_place, stream);
     } else {
         if (nsplit != 1 && nsplit != 2 && nsplit != 4) return KDA_ERR_ARG;
         if (nsplit > 1 && (D != 128 || in_place)) return KDA_ERR_ARG;
@@ -197,7 +203,7 @@ int run_gated(const GatedCall& c, bool layer) {
     }
     kda::StepArgs a{};
     a.M = c.M; a.H = c.H; a.D = c.D; a.state_dtype = c.sdt;
-    a.nsplit = layer ? 1 : choose_split(c.M, c.H, c.D, c.sdt, c.cout == c.cin);
+    a.nsplit = layer ? 1 : choose_split(c.M, c.H, c.D, c.sdt, c.cout == c.cin, c.stream);
     a.state = c.state; a.x = c.x; a.conv_w = c.w; a.conv_in = c.cin; a.conv_out = c.cout;
     a.scale = c.scale; a.o = c.out; a.stream = c.stream;
     a.fgate = c.fgate; a.A_log = c.A_log; a.dt_bias = c.dt_bias; a.beta_logit = c.blogit;
@@ -289,17 +295,19 @@ int kda_decode_multi(int T, int M, int H, int D, int state_dtype, void* state, c
     return map_hip(kda::launch_decode_multi(a));
 }
 
-int kda_prefill_gated(int L, int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
-                      const void* conv_w, const void* conv_in, void* conv_out, const void* f_gate,
-                      const float* A_log, const float* dt_bias, const void* beta_logit,
-                      float gate_lower_bound, float scale, void* o, void* stream) {
+// Host validation shared by the prefill entry points; fills `a` and the
+// input ranges (for the workspace's alias check).
+static int check_prefill(int L, int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                         const void* conv_w, const void* conv_in, void* conv_out, const void* f_gate,
+                         const float* A_log, const float* dt_bias, const void* beta_logit, float gate_lower_bound,
+                         float scale, void* o, void* stream, kda::StepArgs* a, Range (&all)[10]) {
     if (L < 0 || L > KDA_MAX_TOKENS) return KDA_ERR_ARG;
     int rc = check_common(M, H, D, state_dtype, scale);
     if (rc != KDA_OK) return rc;
     if (D != 128) return KDA_ERR_SHAPE;
     if (!(isfinite(gate_lower_bound) && gate_lower_bound >= -5.0f && gate_lower_bound < 0.0f))
         return KDA_ERR_ARG;
-    if (M == 0 || L == 0) return KDA_OK;
+    if (M == 0 || L == 0) return -1;        // nothing to do
     const void* need[] = {state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt_bias, beta_logit, o};
     for (const void* p : need)
         if (!p) return KDA_ERR_NULL;
@@ -323,13 +331,72 @@ int kda_prefill_gated(int L, int M, int H, int D, int state_dtype, void* state, 
         if (i == 2 && conv_out == conv_in) continue;
         if (overlap(rco, inputs[i])) return KDA_ERR_ALIAS;
     }
-    kda::StepArgs a{};
-    a.M = M; a.H = H; a.D = D; a.T = L; a.state_dtype = state_dtype; a.nsplit = 0;
-    a.state = state; a.x = x_qkv; a.conv_w = conv_w; a.conv_in = conv_in; a.conv_out = conv_out;
-    a.fgate = f_gate; a.A_log = A_log; a.dt_bias = dt_bias; a.beta_logit = beta_logit;
-    a.gate_kind = KDA_GATE_BOUNDED; a.lower_bound = gate_lower_bound; a.scale = scale; a.o = o;
-    a.stream = stream;
+    for (int i = 0; i < 7; ++i) all[i] = inputs[i];
+    all[7] = rs;
+    all[8] = ro;
+    all[9] = rco;
+    *a = kda::StepArgs{};
+    a->M = M; a->H = H; a->D = D; a->T = L; a->state_dtype = state_dtype; a->nsplit = 0;
+    a->state = state; a->x = x_qkv; a->conv_w = conv_w; a->conv_in = conv_in; a->conv_out = conv_out;
+    a->fgate = f_gate; a->A_log = A_log; a->dt_bias = dt_bias; a->beta_logit = beta_logit;
+    a->gate_kind = KDA_GATE_BOUNDED; a->lower_bound = gate_lower_bound; a->scale = scale; a->o = o;
+    a->stream = stream;
+    return KDA_OK;
+}
+
+int kda_prefill_gated(int L, int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                      const void* conv_w, const void* conv_in, void* conv_out, const void* f_gate,
+                      const float* A_log, const float* dt_bias, const void* beta_logit,
+                      float gate_lower_bound, float scale, void* o, void* stream) {
+    kda::StepArgs a;
+    Range all[10];
+    const int rc = check_prefill(L, M, H, D, state_dtype, state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log,
+                                 dt_bias, beta_logit, gate_lower_bound, scale, o, stream, &a, all);
+    if (rc == -1) return KDA_OK;
+    if (rc != KDA_OK) return rc;
     return map_hip(kda::launch_prefill(a));
+}
+
+size_t kda_prefill_workspace_bytes(int L, int M, int H, int D) {
+    if (L <= 0 || M <= 0 || H <= 0 || D != 128 || L > KDA_MAX_TOKENS) return 0;
+    const long long chunks = (L + 15) / 16;
+    const long long n = chunks * (long long)M * H;
+    if (n > (1LL << 40) / (long long)kda::prefill_record_bytes()) return 0;
+    return (size_t)n * kda::prefill_record_bytes();
+}
+
+int kda_prefill_gated_ws(int L, int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                         const void* conv_w, const void* conv_in, void* conv_out, const void* f_gate,
+                         const float* A_log, const float* dt_bias, const void* beta_logit,
+                         float gate_lower_bound, float scale, void* o, void* workspace, size_t workspace_bytes,
+                         int passes, void* stream) {
+    if (passes < 0 || passes > 2) return KDA_ERR_ARG;
+    kda::StepArgs a;
+    Range all[10];
+    const int rc = check_prefill(L, M, H, D, state_dtype, state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log,
+                                 dt_bias, beta_logit, gate_lower_bound, scale, o, stream, &a, all);
+    if (rc == -1) return KDA_OK;
+    if (rc != KDA_OK) return rc;
+    const long units = (long)M * H;
+    if (passes != 1) {
+        // checked whatever the choice, so that validity does not depend on the device
+        if (!workspace) return KDA_ERR_NULL;
+        if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+        const size_t full = kda_prefill_workspace_bytes(L, M, H, D);
+        if (full == 0) return KDA_ERR_ARG;
+        size_t need = (size_t)units * kda::prefill_record_bytes();
+        if (state_dtype == KDA_STATE_BF16 && workspace_bytes < full) need += kda::prefill_state_stage_bytes(M, H);
+        if (workspace_bytes < need) return KDA_ERR_ARG;
+        const Range rw = span(workspace, workspace_bytes);
+        for (const Range& r : all)
+            if (overlap(rw, r)) return KDA_ERR_ALIAS;
+    }
+    const int ncu = stream_cus(stream);
+    // the two-pass form while the heads alone leave most CUs idle; above
+    // that, one workgroup per head already fills the device
+    const bool two = passes == 2 || (passes == 0 && units * 2 <= ncu);
+    if (!two) return map_hip(kda::launch_prefill(a));
+    return map_hip(kda::launch_prefill_ws(a, workspace, workspace_bytes, ncu));
 }
 
 int kda_conv_step(int M, int C, const void* x, const void* conv_w, const void* conv_in,
@@ -374,7 +441,7 @@ int kda_recurrent_step(int M, int H, int D, int state_dtype, void* state, const 
     if (overlap(rs, ro)) return KDA_ERR_ALIAS;
     kda::StepArgs a{};
     a.M = M; a.H = H; a.D = D; a.state_dtype = state_dtype;
-    a.nsplit = choose_split(M, H, D, state_dtype, false);
+    a.nsplit = choose_split(M, H, D, state_dtype, false, stream);
     a.state = state; a.qkv = qkv; a.alpha = alpha; a.beta = beta; a.scale = scale; a.o = o;
     a.stream = stream;
     return map_hip(kda::launch_recurrent_step(a));

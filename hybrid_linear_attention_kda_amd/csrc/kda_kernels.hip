@@ -887,15 +887,26 @@ hipError_t launch_conv_step(int M, int C, const void* x, const void* w, const vo
                            (hipStream_t)stream);
 }
 
-int device_cu_count() {
+int device_cu_count(int dev) {
     static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 0) return 0;
     if (dev < 64 && cached[dev] > 0) return cached[dev];
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
     if (dev < 64) cached[dev] = n;
     return n;
+}
+
+int stream_cu_count(void* stream) {
+    int dev = 0;
+    if (stream) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice((hipStream_t)stream, &d) != hipSuccess) return 0;
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return 0;
+    }
+    return device_cu_count(dev);
 }
 
 }  // namespace kda

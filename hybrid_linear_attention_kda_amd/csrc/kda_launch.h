@@ -42,10 +42,20 @@ hipError_t launch_decode_step_gated(const StepArgs& a);
 hipError_t launch_layer_step(const StepArgs& a);
 hipError_t launch_decode_multi(const StepArgs& a);
 hipError_t launch_prefill(const StepArgs& a);
+// two-pass prefill over a workspace of ws_bytes (already validated); ncu =
+// compute units of the device the stream runs on
+hipError_t launch_prefill_ws(const StepArgs& a, void* ws, size_t ws_bytes, int ncu);
+// bytes of one (stream, head, chunk) record of the two-pass prefill
+size_t prefill_record_bytes();
+// f32 copy of the state kept between segments for bf16 storage
+size_t prefill_state_stage_bytes(int M, int H);
 hipError_t launch_conv_step(int M, int C, const void* x, const void* w, const void* cin,
                             void* cout, float* y, void* stream);
 
-// Compute units of the current device (0 if unknown).
-int device_cu_count();
+// Compute units of device `dev` (0 if unknown).
+int device_cu_count(int dev);
+// Compute units of the device `stream` belongs to (NULL: the current
+// device); 0 if unknown.
+int stream_cu_count(void* stream);
 
 }  // namespace kda

@@ -609,6 +609,600 @@ void prefill_kernel(const Ptrs p, const int L)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Two-pass form.  "GLM-5.3 deep dive" 8.2.5 computes each chunk's intra-chunk
+// matrices without the state (parallel over chunks) and carries only the
+// state from chunk to chunk (sequential).  Pass 1 (prep_kernel) does phases 1
+// to 3 for every (stream, head, chunk) at once -- conv + SiLU, gate, beta,
+// norms, A, P and both solves -- and writes a record per chunk; pass 2
+// (scan_kernel) sweeps each head's chunks in order doing only phases 4 and 5.
+// A single long prompt then fills the device in pass 1, and pass 2's serial
+// chain holds no input or solve work.
+//
+// Record of one (stream, head, chunk), in 16-byte units, each array in the
+// fragment order pass 2 reads (lane-major, so a wave's read is contiguous):
+//   Wp [4 kb][3 piece][64 lane]   -W split three ways, A operand of W S
+//   Gq [4 kb][2 piece][64 lane]   Gamma . q^ split two ways, A operand of (Gamma . Q) S
+//   Kt [3 piece][8 mt][2 hf][16]  (gamma_C / Gamma) . k^ split three ways, A operand of the update
+//   P  [64 lane]                  Tril((Gamma . q^)(k^ / Gamma)^T) as the f32 MFMA A operand
+//   Gm [32]                       gamma_C, 4 channels per unit
+//   U  [8 ct][64 lane]            U of column tile ct, the D layout of a 16 x 16 tile
+namespace {
+constexpr int R_WP = 0;
+constexpr int R_GQ = R_WP + 4 * 3 * 64;
+constexpr int R_KT = R_GQ + 4 * 2 * 64;
+constexpr int R_P = R_KT + 3 * 8 * 2 * 16;
+constexpr int R_GM = R_P + 64;
+constexpr int R_SHARED = R_GM + 32;     // the part every column tile reads
+constexpr int R_U = R_SHARED;
+constexpr int R_SIZE = R_U + 8 * 64;    // 2656 units = 42,496 bytes
+
+}  // namespace
+
+size_t prefill_record_bytes() { return (size_t)R_SIZE * 16; }
+
+namespace {
+
+struct PrepSmem {
+    float kh[PC][LS];              // k^; after the solve, -W
+    float vv[PC][LS];              // v; after the solve, U
+    float eg[PC][LS];              // Gamma
+    float qi[2][PC][LS];           // [0] q^ (normalised, scaled), [1] 1 / Gamma
+    float Z[2][PC][LT];            // as PrefillSmem
+    float P[2][PC][LT];
+    float gam[PD];
+    float beta[PC];
+};
+
+// Pass 1: one workgroup of 4 waves per (group of cpw chunks, stream, head) of
+// a segment of nch chunks starting at chunk c0; block b = (group, m, h)
+// row-major.  Per chunk, phases 1 to 3 as prefill_kernel; the raw inputs of
+// the group's next chunk are requested while the current one runs phases 2
+// and 3, and the three raw inputs before each chunk are carried from the
+// previous one (read from x, or for the sequence's first chunk from the
+// cached taps, at the start of the group).  Chunk cl of the segment writes
+// record (cl, m, h).
+__global__ __launch_bounds__(PNT, 3)
+void prep_kernel(const Ptrs p, const int L, const int M, const int c0, const int nch, const int cpw,
+                 u32x4* __restrict__ ws)
+{
+    __shared__ PrepSmem sm;
+    const int b = (int)blockIdx.x;
+    const int h = b % p.H, mg = b / p.H, m = mg % M, grp = mg / M;
+    const int cl0 = grp * cpw, cl1 = min(nch, cl0 + cpw);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const size_t HD = (size_t)p.H * PD, C3 = 3 * HD;
+
+    const bool qk = wv < 2;
+    const int vc = 64 * (wv & 1) + lane;
+    const size_t ch = qk ? (size_t)wv * HD + (size_t)h * PD + 2 * lane : 2 * HD + (size_t)h * PD + vc;
+    const size_t fc = (size_t)h * PD + vc;
+    const uint16_t* const s1 = p.x + (size_t)m * L * C3 + ch;
+    const uint16_t* const s2 = p.fgate + (size_t)m * L * HD + fc;
+    const uint16_t* const ci = p.conv_in + (size_t)m * 3 * C3 + ch;
+    const float eA = expf(p.A_log[h]);
+    const float lb = p.lower_bound;
+
+    // conv weights and the three raw inputs before the group's first chunk
+    float cw[8], a0, a1, a2, b0 = 0.f, b1 = 0.f, b2 = 0.f, db = 0.f;
+    {
+        const int t0 = (c0 + cl0) * PC;
+        uint32_t prev[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int pos = t0 - 3 + k;
+            const uint16_t* src = pos < 0 ? ci + (size_t)(3 + pos) * C3 : s1 + (size_t)pos * C3;
+            prev[k] = qk ? *reinterpret_cast<const uint32_t*>(src) : (uint32_t)*src;
+        }
+        a0 = bf16_lo(prev[0]); a1 = bf16_lo(prev[1]); a2 = bf16_lo(prev[2]);
+        if (qk) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(p.conv_w + 4 * ch);
+            cw[0] = bf16_lo(w.x); cw[1] = bf16_hi(w.x); cw[2] = bf16_lo(w.y); cw[3] = bf16_hi(w.y);
+            cw[4] = bf16_lo(w.z); cw[5] = bf16_hi(w.z); cw[6] = bf16_lo(w.w); cw[7] = bf16_hi(w.w);
+            b0 = bf16_hi(prev[0]); b1 = bf16_hi(prev[1]); b2 = bf16_hi(prev[2]);
+        } else {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(p.conv_w + 4 * ch);
+            cw[0] = bf16_lo(w.x); cw[1] = bf16_hi(w.x); cw[2] = bf16_lo(w.y); cw[3] = bf16_hi(w.y);
+            cw[4] = cw[5] = cw[6] = cw[7] = 0.f;
+            db = p.dt_bias[fc];
+        }
+    }
+
+    // raw inputs of one chunk (the last token again past the end of the
+    // sequence; its results are masked out): q/k waves two channels per
+    // 32-bit load, v/gate waves the v and forget-gate channel; every lane
+    // the write-strength logit of token lane % 16
+    uint32_t raw[PC], rawf[PC], rawb;
+    auto fetch = [&](int t0) {
+        const int last = min(PC, L - t0) - 1;
+#pragma unroll
+        for (int j = 0; j < PC; ++j) {
+            const size_t t = (size_t)(t0 + min(j, last));
+            raw[j] = qk ? *reinterpret_cast<const uint32_t*>(s1 + t * C3) : (uint32_t)s1[t * C3];
+            rawf[j] = qk ? 0u : (uint32_t)s2[t * HD];
+        }
+        rawb = p.blogit[((size_t)m * L + t0 + min(lane & (PC - 1), last)) * p.H + h];
+    };
+    fetch((c0 + cl0) * PC);
+
+    for (int cl = cl0; cl < cl1; ++cl) {
+        const int t0 = (c0 + cl) * PC;
+        const int n = min(PC, L - t0);
+        u32x4* const rec = ws + ((size_t)cl * M + m) * p.H * R_SIZE + (size_t)h * R_SIZE;
+
+        // ---- 1. inputs ----
+        if (qk) {
+            float z0[PC], z1[PC];
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+                const float x0 = bf16_lo(raw[j]), x1 = bf16_hi(raw[j]);
+                float y0 = cw[0] * a0;
+                y0 = fmaf(cw[1], a1, y0);
+                y0 = fmaf(cw[2], a2, y0);
+                y0 = fmaf(cw[3], x0, y0);
+                float y1 = cw[4] * b0;
+                y1 = fmaf(cw[5], b1, y1);
+                y1 = fmaf(cw[6], b2, y1);
+                y1 = fmaf(cw[7], x1, y1);
+                z0[j] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
+                z1[j] = j < n ? y1 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y1)) : 0.f;
+                a0 = a1; a1 = a2; a2 = x0;
+                b0 = b1; b1 = b2; b2 = x1;
+            }
+            float (*dst)[LS] = wv == 0 ? sm.qi[0] : sm.kh;
+            float ss[PC];
+#pragma unroll
+            for (int j = 0; j < PC; ++j) ss[j] = fmaf(z0[j], z0[j], z1[j] * z1[j]);
+            const float tot = wave_sum16(ss, lane);
+            const float rn = (wv == 0 ? p.scale : 1.0f) * rsqrtf(tot + 1e-6f);
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+                const float rj = lane_value(rn, sum16_lane(j));
+                *reinterpret_cast<float2*>(&dst[j][2 * lane]) = make_float2(z0[j] * rj, z1[j] * rj);
+            }
+        } else {
+            float e = 1.f;
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+                const float x0 = bf16_lo(raw[j]);
+                float y0 = cw[0] * a0;
+                y0 = fmaf(cw[1], a1, y0);
+                y0 = fmaf(cw[2], a2, y0);
+                y0 = fmaf(cw[3], x0, y0);
+                sm.vv[j][vc] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
+                a0 = a1; a1 = a2; a2 = x0;
+                const float g = lb * __builtin_amdgcn_rcpf(1.0f + exp_fast(-eA * (bf16_lo(rawf[j]) + db)));
+                e *= j < n ? exp_fast(g) : 1.f;
+                sm.eg[j][vc] = e;
+                sm.qi[1][j][vc] = __builtin_amdgcn_rcpf(e);
+            }
+            sm.gam[vc] = e;
+            if (wv == 3 && lane < PC)
+                sm.beta[lane] = lane < n ? __builtin_amdgcn_rcpf(1.0f + exp_fast(-bf16_lo(rawb))) : 0.0f;
+        }
+        if (cl + 1 < cl1) fetch(t0 + PC);
+        lds_barrier();
+
+        // ---- 2. A and P; the record's Gamma . q^ and (gamma_C / Gamma) . k^ pieces ----
+        {
+            const int cb = 64 * (wv & 1);
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            if (wv < 2) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = cb + 16 * g4 + 4 * q;
+                    const f32x4 k4 = lds4(&sm.kh[l16][c]), e4 = lds4(&sm.eg[l16][c]), i4 = lds4(&sm.qi[1][l16][c]);
+                    acc0 = mfma16(k4.x * e4.x, k4.x * i4.x, acc0);
+                    acc1 = mfma16(k4.y * e4.y, k4.y * i4.y, acc1);
+                    acc0 = mfma16(k4.z * e4.z, k4.z * i4.z, acc0);
+                    acc1 = mfma16(k4.w * e4.w, k4.w * i4.w, acc1);
+                }
+                *reinterpret_cast<f32x4*>(&sm.Z[wv & 1][l16][4 * g4]) = acc0 + acc1;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = cb + 16 * g4 + 4 * q;
+                    const f32x4 k4 = lds4(&sm.kh[l16][c]), i4 = lds4(&sm.qi[1][l16][c]);
+                    const f32x4 q4 = lds4(&sm.qi[0][l16][c]), e4 = lds4(&sm.eg[l16][c]);
+                    acc0 = mfma16(k4.x * i4.x, q4.x * e4.x, acc0);
+                    acc1 = mfma16(k4.y * i4.y, q4.y * e4.y, acc1);
+                    acc0 = mfma16(k4.z * i4.z, q4.z * e4.z, acc0);
+                    acc1 = mfma16(k4.w * i4.w, q4.w * e4.w, acc1);
+                }
+                f32x4 d = acc0 + acc1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g4 + r > l16) d[r] = 0.f;
+                *reinterpret_cast<f32x4*>(&sm.P[wv & 1][l16][4 * g4]) = d;
+            }
+            {
+                const int kb = tid >> 6, ln = tid & 63, tk = ln & 15, cq = 32 * kb + 4 * (ln >> 4);
+                u32x4 pc[3];
+                split8(lds4(&sm.qi[0][tk][cq]) * lds4(&sm.eg[tk][cq]),
+                       lds4(&sm.qi[0][tk][cq + 16]) * lds4(&sm.eg[tk][cq + 16]), pc);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) rec[R_GQ + (kb * 2 + q) * 64 + ln] = pc[q];
+            }
+            {
+                const int mt = tid >> 5, hf = (tid >> 4) & 1, k = 16 * mt + (tid & 15);
+                const float gk = sm.gam[k];
+                float v[8];
+#pragma unroll
+                for (int s2i = 0; s2i < 8; ++s2i) v[s2i] = sm.kh[8 * hf + s2i][k] * (gk * sm.qi[1][8 * hf + s2i][k]);
+                u32x4 pc[3];
+                split8(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}, pc);
+#pragma unroll
+                for (int q = 0; q < 3; ++q) rec[R_KT + ((q * 8 + mt) * 2 + hf) * 16 + (tid & 15)] = pc[q];
+            }
+        }
+        lds_barrier();
+
+        // ---- 3. (I + A) W = Diag(beta)(Gamma . K), (I + A) U = Diag(beta) V ----
+        {
+            const int col = tid & (PD - 1);
+            float (*X)[LS] = wv < 2 ? sm.kh : sm.vv;
+            float cv[PC];
+            if (wv < 2) {
+#pragma unroll
+                for (int j = 0; j < PC; ++j) cv[j] = sm.kh[j][col] * sm.eg[j][col];
+            } else {
+#pragma unroll
+                for (int j = 0; j < PC; ++j) cv[j] = sm.vv[j][col];
+            }
+            solve_column(cv, sm.Z, sm.beta, lane);
+            const float sg = wv < 2 ? -1.0f : 1.0f;
+#pragma unroll
+            for (int j = 0; j < PC; ++j) X[j][col] = cv[j] * sg;
+        }
+        lds_barrier();
+
+        // ---- the record's -W pieces, U tiles, P and gamma_C ----
+        {
+            const int kb = wv;
+            u32x4 wp[3];
+            split8(lds4(&sm.kh[l16][32 * kb + 4 * g4]), lds4(&sm.kh[l16][32 * kb + 16 + 4 * g4]), wp);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) rec[R_WP + (kb * 3 + q) * 64 + lane] = wp[q];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int ct = 2 * wv + i, col = 16 * ct + l16;
+                const f32x4 u = {sm.vv[4 * g4][col], sm.vv[4 * g4 + 1][col], sm.vv[4 * g4 + 2][col],
+                                 sm.vv[4 * g4 + 3][col]};
+                rec[R_U + ct * 64 + lane] = __builtin_bit_cast(u32x4, u);
+            }
+            if (wv == 0) {
+                const f32x4 p4 = lds4(&sm.P[0][l16][4 * g4]) + lds4(&sm.P[1][l16][4 * g4]);
+                rec[R_P + lane] = __builtin_bit_cast(u32x4, p4);
+            } else if (wv == 1 && lane < 32) {
+                rec[R_GM + lane] = __builtin_bit_cast(u32x4, lds4(&sm.gam[4 * lane]));
+            }
+        }
+        // the next chunk's phase 1 overwrites what the record was read from
+        lds_barrier();
+    }
+}
+
+// Pass 2: per workgroup TPW column tiles of head (m, h), two waves per tile,
+// for chunks [c0, c0 + nch).  Tile ct = TPW * split + i covers value columns
+// [16 ct, 16 ct + 16); its two waves split the key rows: wave half hs holds
+// rows [64 hs, 64 hs + 64) of the tile (state blocks kb = 2 hs, 2 hs + 1) in
+// the D layout of the 16 x 16 MFMAs -- lane (l16, g4) holds rows
+// 16 mt + 4 g4 + r, mt = 4 hs .. 4 hs + 3, of column 16 ct + l16.  Per chunk
+// each wave forms its rows' share of W S (the half-0 wave starting from U)
+// and of (Gamma . Q) S; the two shares meet in LDS after a barrier and both
+// waves add them in the same order, so both hold the same Delta; the half-0
+// wave writes the outputs, and each wave updates its own rows.
+// The shared part of each chunk's record is staged in LDS, double-buffered:
+// a chunk's part is fetched into registers two chunks ahead and written to
+// the other buffer at the end of the chunk before it (two barriers per
+// chunk).
+// The state comes from `sin` and goes to `sout`: the caller's state (type
+// TS) at the ends of the call, f32 in the workspace between segments.
+template <int TPW>
+struct ScanSmem {
+    // the shared record part, rounded up to whole staging rounds of the
+    // workgroup's threads (the extra units are the start of the U tiles,
+    // inside the record, and are not read from LDS)
+    u32x4 rec[2][(R_SHARED + TPW * 128 - 1) / (TPW * 128) * (TPW * 128)];
+    f32x4 part[2 * TPW][2][64];        // [wave][W S share, (Gamma . Q) S share][lane]
+    u32x4 dp[2 * TPW][3][2][16];       // Delta pieces [wave][piece][token half][column]
+};
+
+template <typename TSI, typename TSO, int TPW>
+__global__ __launch_bounds__(TPW * 128)
+void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int nch,
+                 const u32x4* __restrict__ ws, const TSI* sin, TSO* sout, const int write_conv)
+{
+    constexpr int NS = 8 / TPW;                        // workgroups per head
+    constexpr int NT = TPW * 128;
+    constexpr int PER = (R_SHARED + NT - 1) / NT;      // 16-byte units each thread stages
+    static_assert(PER * NT <= R_SIZE, "staging stays inside the record");
+    __shared__ ScanSmem<TPW> sm;
+    // XCD-aware: workgroups go to the 8 XCDs round robin; the NS workgroups of
+    // a head sit on one XCD, so they read its records through one L2
+    const int units = M * p.H;
+    int unit, split;
+    {
+        const int b = (int)blockIdx.x;
+        const int full = units >> 3;
+        if (NS > 1 && b < full * 8 * NS) {
+            const int g = b / (8 * NS), r = b - g * 8 * NS;
+            unit = g * 8 + (r & 7);
+            split = r >> 3;
+        } else {
+            const int bb = b - (NS > 1 ? full * 8 * NS : 0);
+            unit = (NS > 1 ? full * 8 : 0) + bb / NS;
+            split = bb - (bb / NS) * NS;
+        }
+    }
+    const int m = unit / p.H, h = unit - m * p.H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hs = wv & 1, ti = wv >> 1;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int ct = TPW * split + ti, col = 16 * ct + l16;
+    const size_t rstride = (size_t)M * p.H * R_SIZE;   // from one chunk's records to the next
+    const u32x4* const rec0 = ws + (size_t)unit * R_SIZE;
+
+    float S[4][4];
+    {
+        const TSI* const st = sin + (size_t)unit * PD * PD;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[mi][r] = load_state_elem(st + (size_t)(16 * (4 * hs + mi) + 4 * g4 + r) * PD + col);
+    }
+
+    // Records are fetched two chunks ahead (their latency from HBM exceeds
+    // a chunk's work): register set 0 holds even chunks, set 1 odd ones,
+    // and the loop runs two chunks per iteration so that both sets stay
+    // compile-time arrays.
+    u32x4 stg0[PER], stg1[PER];
+    f32x4 un0 = f32x4{0.f, 0.f, 0.f, 0.f}, un1 = un0;
+    auto fetch = [&](u32x4 (&stg)[PER], f32x4& un, int c) {
+        const u32x4* const rc = rec0 + (size_t)c * rstride;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) stg[i] = rc[tid + i * NT];
+        if (hs == 0) un = __builtin_bit_cast(f32x4, rc[R_U + ct * 64 + lane]);
+    };
+    auto put = [&](const u32x4 (&stg)[PER], int buf) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) sm.rec[buf][tid + i * NT] = stg[i];
+    };
+
+    // chunk c from LDS buffer c & 1 with U from `uc`; `nxt` (chunk c + 1's
+    // record, fetched a chunk ago) goes to the other buffer at the end, and
+    // `cur` (free once chunk c's record is in LDS) takes chunk c + 2's
+    auto chunk = [&](int c, u32x4 (&cur)[PER], f32x4& ucur, const u32x4 (&nxt)[PER]) {
+        const int buf = c & 1;
+        const u32x4* const R = sm.rec[buf];
+        const int t0 = (c0 + c) * PC;
+        const f32x4 uc = ucur;
+        if (c + 2 < nch) fetch(cur, ucur, c + 2);
+
+        // ---- 4. this wave's share of Delta = U - W S and of (Gamma . Q) S ----
+        u32x4 wp[2][3], gp[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int kb = 2 * hs + i;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) wp[i][q] = R[R_WP + (kb * 3 + q) * 64 + lane];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) gp[i][q] = R[R_GQ + (kb * 2 + q) * 64 + lane];
+        }
+        f32x4 dk[2], ok = {0.f, 0.f, 0.f, 0.f};
+        dk[0] = uc;
+        dk[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            u32x4 sb[3];
+            split8(f32x4{S[2 * i][0], S[2 * i][1], S[2 * i][2], S[2 * i][3]},
+                   f32x4{S[2 * i + 1][0], S[2 * i + 1][1], S[2 * i + 1][2], S[2 * i + 1][3]}, sb);
+#pragma unroll
+            for (int pr = 0; pr < 6; ++pr) {
+                dk[i] = mfma_bf16(wp[i][PAIR_A[pr]], sb[PAIR_B[pr]], dk[i]);
+                if (pr < 3) ok = mfma_bf16(gp[i][PAIR_A[pr]], sb[PAIR_B[pr]], ok);
+            }
+        }
+        // the update's operands from the record, read before the barrier
+        const int hh = g4 & 1, sel = g4 >> 1;
+        u32x4 ka[4][3];
+        f32x4 gm[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int mt = 4 * hs + mi;
+            gm[mi] = __builtin_bit_cast(f32x4, R[R_GM + 4 * mt + g4]);
+#pragma unroll
+            for (int mm = 0; mm < 3; ++mm) {
+                const int q = sel ? PAIR_A[2 * mm + 1] : PAIR_A[2 * mm];
+                ka[mi][mm] = R[R_KT + ((q * 8 + mt) * 2 + hh) * 16 + l16];
+            }
+        }
+        sm.part[wv][0][lane] = dk[0] + dk[1];
+        sm.part[wv][1][lane] = ok;
+        lds_barrier();
+        // both waves of the tile add the two shares in the same order
+        const f32x4 dacc = sm.part[wv & ~1][0][lane] + sm.part[wv | 1][0][lane];
+        {
+            uint32_t p0a, p1a, p2a, p0b, p1b, p2b;
+            split2(dacc[0], dacc[1], p0a, p1a, p2a);
+            split2(dacc[2], dacc[3], p0b, p1b, p2b);
+            u32x2* const dst = reinterpret_cast<u32x2*>(&sm.dp[wv][0][g4 >> 1][l16]) + (g4 & 1);
+            constexpr int PIECE = sizeof(sm.dp[0][0]) / sizeof(u32x2);
+            dst[0] = u32x2{p0a, p0b};
+            dst[PIECE] = u32x2{p1a, p1b};
+            dst[2 * PIECE] = u32x2{p2a, p2b};
+        }
+        lds_wave_fence();
+
+        // ---- 5. S' = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta; O = (Gamma . Q) S + P Delta (half 0) ----
+        {
+            u32x4 db[3];
+#pragma unroll
+            for (int mm = 0; mm < 3; ++mm) db[mm] = sm.dp[wv][sel ? PAIR_B[2 * mm + 1] : PAIR_B[2 * mm]][hh][l16];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                f32x4 acc = {S[mi][0] * gm[mi].x, S[mi][1] * gm[mi].y, S[mi][2] * gm[mi].z, S[mi][3] * gm[mi].w};
+#pragma unroll
+                for (int mm = 0; mm < 3; ++mm) acc = mfma_bf16(ka[mi][mm], db[mm], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[mi][r] = acc[r];
+            }
+        }
+        {
+            // both waves form the tile's outputs; each stores two of a lane's
+            // four tokens
+            f32x4 oacc = sm.part[wv & ~1][1][lane] + sm.part[wv | 1][1][lane];
+            const f32x4 p4 = __builtin_bit_cast(f32x4, R[R_P + lane]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) oacc = mfma16(p4[kk], dacc[kk], oacc);
+            uint16_t* const ob = p.o + (((size_t)m * L + t0) * p.H + h) * PD + col;
+            const size_t ts = (size_t)p.H * PD;
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int t = 4 * g4 + 2 * hs + rr;
+                const float v = hs ? oacc[2 + rr] : oacc[rr];
+                if (t0 + t < L) ob[(size_t)t * ts] = (uint16_t)(cvt_pk_bf16(v, 0.0f) & 0xffffu);
+            }
+        }
+        // the next chunk's shared record part into the other buffer; the
+        // shares and Delta pieces are rewritten only after the barrier
+        if (c + 1 < nch) put(nxt, buf ^ 1);
+        lds_barrier();
+    };
+
+    fetch(stg0, un0, 0);
+    if (nch > 1) fetch(stg1, un1, 1);
+    put(stg0, 0);
+    lds_barrier();
+    for (int c = 0; c < nch; c += 2) {
+        chunk(c, stg0, un0, stg1);
+        if (c + 1 < nch) chunk(c + 1, stg1, un1, stg0);
+    }
+
+    {
+        int so = (64 * hs + 4 * g4) * PD + col;
+        asm volatile("" : "+v"(so));
+        TSO* const st = sout + (size_t)unit * PD * PD + so;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) store_state_elem(st + (16 * mi + r) * PD, S[mi][r]);
+    }
+    // conv state after the sequence (last segment only): the raw inputs of
+    // positions L-3, L-2, L-1 of the workgroup's share of the head's q, k, v
+    // channels, one channel per thread; a position < 0 is a cached tap, read
+    // by the same thread before it overwrites it
+    if (write_conv) {
+        constexpr int CPS = PD / NS;                   // channels of each tensor per workgroup
+        static_assert(3 * CPS <= NT, "one thread per channel");
+        if (tid < 3 * CPS) {
+            const size_t HD = (size_t)p.H * PD, C3 = 3 * HD;
+            const int tensor = tid / CPS, c = split * CPS + (tid - tensor * CPS);
+            const size_t chn = (size_t)tensor * HD + (size_t)h * PD + c;
+            uint16_t v3[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int pos = L - 3 + k;
+                v3[k] = pos < 0 ? p.conv_in[(size_t)m * 3 * C3 + (size_t)(3 + pos) * C3 + chn]
+                                : p.x[((size_t)m * L + pos) * C3 + chn];
+            }
+            uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + chn;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) co[(size_t)k * C3] = v3[k];
+        }
+    }
+}
+
+}  // namespace
+
+// Two-pass prefill over a caller workspace: the sequence runs in segments of
+// as many chunks as the workspace holds records for (every stream and head
+// of a chunk at once), pass 1 then pass 2 per segment.  Between segments the
+// state is carried in f32: in the caller's state for f32 storage, in the
+// workspace after the records for bf16 storage (so bf16 state is rounded
+// once, at the end of the call, however many segments run).
+template <typename TSI, typename TSO>
+static hipError_t launch_scan(int tpw, const Ptrs& p, int L, int M, int c0, int nch, const u32x4* ws,
+                              const void* sin, void* sout, int write_conv, int units, hipStream_t stream) {
+    const TSI* si = static_cast<const TSI*>(sin);
+    TSO* so = static_cast<TSO*>(sout);
+    void* args[] = {(void*)&p, (void*)&L, (void*)&M, (void*)&c0, (void*)&nch, (void*)&ws, (void*)&si, (void*)&so,
+                    (void*)&write_conv};
+    const void* fn = tpw == 2 ? reinterpret_cast<const void*>(&scan_kernel<TSI, TSO, 2>)
+                              : reinterpret_cast<const void*>(&scan_kernel<TSI, TSO, 4>);
+    return hipLaunchKernel(fn, dim3((unsigned)(units * (8 / tpw))), dim3(tpw * 128), args, 0, stream);
+}
+
+size_t prefill_state_stage_bytes(int M, int H) { return (size_t)M * H * PD * PD * sizeof(float); }
+
+hipError_t launch_prefill_ws(const StepArgs& a, void* ws, size_t ws_bytes, int ncu) {
+    if (a.D != PD) return hipErrorInvalidValue;
+    Ptrs p = make_ptrs(a);
+    const int L = a.T, M = a.M;
+    const int units = M * a.H;
+    const int nchunks = (L + PC - 1) / PC;
+    const size_t per_chunk = (size_t)units * R_SIZE * 16;
+    const bool bf16 = a.state_dtype != 0;
+    // records of one segment; bf16 state also needs its f32 stage when the
+    // sequence takes more than one segment
+    size_t seg = ws_bytes / per_chunk;
+    if ((long)seg < nchunks && bf16) {
+        const size_t stage = prefill_state_stage_bytes(M, a.H);
+        seg = ws_bytes > stage ? (ws_bytes - stage) / per_chunk : 0;
+    }
+    if (seg < 1) return hipErrorInvalidValue;
+    const int seg_chunks = (int)((long)seg < nchunks ? (long)seg : nchunks);
+    const int nseg = (nchunks + seg_chunks - 1) / seg_chunks;
+    u32x4* const rec = static_cast<u32x4*>(ws);
+    float* const stage = bf16 ? reinterpret_cast<float*>(static_cast<char*>(ws) + (size_t)seg_chunks * per_chunk)
+                              : static_cast<float*>(a.state);
+    // column tiles per pass-2 workgroup: 2 (one workgroup of 4 waves, one
+    // per SIMD, on each CU) while that gives at most a workgroup per CU,
+    // else 4 (8 waves; their registers allow one workgroup per CU)
+    const long want = ncu > 0 ? ncu : 256;
+    const int tpw = (long)units * 4 <= want ? 2 : 4;
+    const hipStream_t stream = (hipStream_t)a.stream;
+    for (int sgi = 0; sgi < nseg; ++sgi) {
+        int c0 = sgi * seg_chunks;
+        const int nch = min(seg_chunks, nchunks - c0);
+        {
+            // chunks per pass-1 workgroup: several (their input latency then
+            // hides behind the previous chunk's work) while the grid still
+            // gives every CU about four rounds of three workgroups
+            const long slots = 12L * want;
+            int cpw = (int)((long)nch * units / slots);
+            cpw = cpw < 1 ? 1 : (cpw > 8 ? 8 : cpw);
+            int Li = L, Mi = M, nchi = nch;
+            u32x4* w = rec;
+            void* args[] = {(void*)&p, (void*)&Li, (void*)&Mi, (void*)&c0, (void*)&nchi, (void*)&cpw, (void*)&w};
+            const long groups = (nch + cpw - 1) / cpw;
+            hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&prep_kernel),
+                                           dim3((unsigned)(groups * units)), dim3(PNT), args, 0, stream);
+            if (e != hipSuccess) return e;
+        }
+        const bool first = sgi == 0, last = sgi == nseg - 1;
+        const void* sin = first ? a.state : static_cast<const void*>(stage);
+        void* sout = last ? a.state : static_cast<void*>(stage);
+        hipError_t e;
+        if (!bf16)
+            e = launch_scan<float, float>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+        else if (first && last)
+            e = launch_scan<uint16_t, uint16_t>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+        else if (first)
+            e = launch_scan<uint16_t, float>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+        else if (last)
+            e = launch_scan<float, uint16_t>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+        else
+            e = launch_scan<float, float>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Two workgroups per head when the heads alone would leave more than half
 // of the CUs idle (the duplicated input, A, P and solve work then costs
 // nothing but otherwise idle CUs) and conv_out is a buffer of its own.
@@ -617,11 +1211,8 @@ hipError_t launch_prefill(const StepArgs& a) {
     Ptrs p = make_ptrs(a);
     int L = a.T;
     void* args[] = {(void*)&p, (void*)&L};
-    int dev = 0, ncu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
+    int ncu = stream_cu_count(a.stream);
+    if (ncu <= 0) ncu = 256;
     const long units = (long)a.M * a.H;
     const bool two = a.nsplit == 0 && a.conv_out != a.conv_in && 2 * units <= ncu;   // nsplit 0: choose
     const bool f32 = a.state_dtype == 0;

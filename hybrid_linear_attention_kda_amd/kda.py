@@ -24,7 +24,8 @@ KDA_GATE_BOUNDED, KDA_GATE_SOFTPLUS = 0, 1
 
 #: every symbol ``include/kda.h`` declares
 EXPORTS = ("kda_decode_step", "kda_decode_step_split", "kda_decode_step_gated",
-           "kda_decode_layer_step", "kda_decode_multi", "kda_prefill_gated", "kda_conv_step",
+           "kda_decode_layer_step", "kda_decode_multi", "kda_prefill_gated", "kda_prefill_gated_ws",
+           "kda_prefill_workspace_bytes", "kda_conv_step",
            "kda_recurrent_step", "kda_status_string", "kda_version")
 
 
@@ -60,6 +61,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_multi.restype = i
     lib.kda_prefill_gated.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, fp, fp, vp, f, f, vp, vp]
     lib.kda_prefill_gated.restype = i
+    lib.kda_prefill_gated_ws.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, fp, fp, vp, f, f, vp, vp,
+                                         ctypes.c_size_t, i, vp]
+    lib.kda_prefill_gated_ws.restype = i
+    lib.kda_prefill_workspace_bytes.argtypes = [i, i, i, i]
+    lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_conv_step.argtypes = [i, i, vp, vp, vp, vp, fp, vp]
     lib.kda_conv_step.restype = i
     lib.kda_recurrent_step.argtypes = [i, i, i, i, vp, fp, fp, fp, f, vp, vp]
@@ -272,11 +278,19 @@ def kda_decode_multi(state, x_qkv, conv_w, conv_in, conv_out, alpha, beta, scale
                                 _stream(dev, stream)))
 
 
+def kda_prefill_workspace_bytes(L: int, M: int, H: int, D: int) -> int:
+    """Workspace for a one-segment kda_prefill_gated_ws call (0: invalid shape)."""
+    return int(load().kda_prefill_workspace_bytes(int(L), int(M), int(H), int(D)))
+
+
 def kda_prefill_gated(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt_bias, beta_logit,
-                      scale, o, lower_bound=-5.0, stream=None):
+                      scale, o, lower_bound=-5.0, stream=None, workspace=None, passes=0):
     """L tokens per stream, chunkwise on matrix cores (see ``kda_prefill_gated``
     in kda.h): x_qkv [M,L,3,H*D] bf16, f_gate [M,L,H*D] bf16, A_log [H] f32,
-    dt_bias [H*D] f32, beta_logit [M,L,H] bf16, o [M,L,H,D] bf16; D = 128."""
+    dt_bias [H*D] f32, beta_logit [M,L,H] bf16, o [M,L,H,D] bf16; D = 128.
+    With ``workspace`` (a contiguous GPU tensor of any dtype) the call goes to
+    ``kda_prefill_gated_ws`` with ``passes`` (0 choose, 1 one pass, 2 two
+    passes)."""
     lib = load()
     if state.dim() != 4 or x_qkv.dim() != 4:
         raise ValueError("state must be [M, H, D, D] and x_qkv [M, L, 3, H*D]")
@@ -295,8 +309,18 @@ def kda_prefill_gated(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt
     _need(dt_bias, "dt_bias", (H * D,), torch.float32, dev)
     _need(beta_logit, "beta_logit", (M, L, H), torch.bfloat16, dev)
     _need(o, "o", (M, L, H, D), torch.bfloat16, dev)
-    _check("kda_prefill_gated",
-           lib.kda_prefill_gated(L, M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w),
-                                 _p(conv_in), _p(conv_out), _p(f_gate), _p(A_log), _p(dt_bias),
-                                 _p(beta_logit), float(lower_bound), float(scale), _p(o),
-                                 _stream(dev, stream)))
+    if workspace is None:
+        _check("kda_prefill_gated",
+               lib.kda_prefill_gated(L, M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w),
+                                     _p(conv_in), _p(conv_out), _p(f_gate), _p(A_log), _p(dt_bias),
+                                     _p(beta_logit), float(lower_bound), float(scale), _p(o),
+                                     _stream(dev, stream)))
+        return
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the state's device")
+    _check("kda_prefill_gated_ws",
+           lib.kda_prefill_gated_ws(L, M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w),
+                                    _p(conv_in), _p(conv_out), _p(f_gate), _p(A_log), _p(dt_bias),
+                                    _p(beta_logit), float(lower_bound), float(scale), _p(o), _p(workspace),
+                                    workspace.numel() * workspace.element_size(), int(passes),
+                                    _stream(dev, stream)))

@@ -17,7 +17,8 @@
  * ---------------------------------------
  * - All array arguments are DEVICE pointers to memory the caller owns.  The
  *   library never allocates, frees, synchronises, or keeps state between
- *   calls.  Every pointer must be 16-byte aligned.
+ *   calls (kda_prefill_gated_ws takes its scratch memory as a caller
+ *   workspace).  Every pointer must be 16-byte aligned.
  * - Arrays are dense, row-major, last index fastest.  "bf16" is the 16-bit
  *   bfloat16 bit pattern (uint16); "f32" is IEEE binary32.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
@@ -35,6 +36,8 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -51,12 +54,12 @@ enum {
     KDA_ERR_HIP = 7     /* the HIP runtime refused the launch                 */
 };
 
-/* Storage type of the recurrent state.  Arithmetic is f32 either way. */
 /* Largest token count per stream of one kda_decode_multi or
  * kda_prefill_gated call (2^30): keeps every token index of the kernels'
  * chunk loops inside int. */
 #define KDA_MAX_TOKENS (1 << 30)
 
+/* Storage type of the recurrent state.  Arithmetic is f32 either way. */
 typedef enum { KDA_STATE_F32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype;
 
 /* Forget-gate forms ("GLM-5.3 deep dive", 8.2.3, the gate as fla computes
@@ -246,6 +249,70 @@ int kda_prefill_gated(int L, int M, int H, int D, int state_dtype,
                       const float *dt_bias, const void *beta_logit,
                       float gate_lower_bound, float scale, void *o,
                       void *stream);
+
+/* Bytes of one (stream, head, 16-token chunk) record of the two-pass prefill. */
+#define KDA_PREFILL_RECORD_BYTES 42496
+
+/*
+ * kda_prefill_workspace_bytes -- workspace that lets kda_prefill_gated_ws run
+ * an L-token call in one segment: ceil(L / 16) * M * H *
+ * KDA_PREFILL_RECORD_BYTES.  0 for an invalid shape (L, M or H < 1, D != 128)
+ * or a size above 2^40.  Smaller workspaces also work (see below).
+ */
+size_t kda_prefill_workspace_bytes(int L, int M, int H, int D);
+
+/*
+ * kda_prefill_gated_ws -- kda_prefill_gated in the two-pass chunk form of
+ * "GLM-5.3 deep dive" 8.2.5 (the intra-chunk work is parallel over chunks;
+ * only the state is carried from chunk to chunk):
+ *   pass 1, one workgroup per (stream, head, chunk): conv + SiLU, gate, beta,
+ *     L2 norms, A = StrictTril(Diag(beta)(Gamma . K)(K / Gamma)^T), the
+ *     output mask P and the solves (I + A) W = Diag(beta)(Gamma . K),
+ *     (I + A) U = Diag(beta) V, written to the workspace as one record per
+ *     chunk;
+ *   pass 2, per (stream, head) and in chunk order: Delta = U - W S,
+ *     O = (Gamma . Q) S + P Delta, S' = Diag(gamma_C) S + ((gamma_C / Gamma)
+ *     . K)^T Delta, with 16 value columns per wave.
+ * A single long prompt (few streams) then occupies the whole device in pass
+ * 1, where kda_prefill_gated's one workgroup per head would leave most CUs
+ * idle.
+ *
+ *  Arguments before `workspace` are those of kda_prefill_gated, with the same
+ *  meaning, layouts, ranges and aliasing rules.
+ *  workspace        DEVICE scratch memory the caller owns, 16-byte aligned,
+ *                   overlapping no other argument; its contents on entry are
+ *                   ignored and on exit unspecified.  Calls that share one
+ *                   workspace must be ordered (same stream).
+ *  workspace_bytes  its size.  With kda_prefill_workspace_bytes(L, M, H, D)
+ *                   or more the call runs as one segment (two launches); a
+ *                   smaller workspace runs the sequence in segments of as
+ *                   many chunks as fit (two launches each), down to
+ *                   M * H * KDA_PREFILL_RECORD_BYTES, plus M * H * 65536
+ *                   bytes for bf16 state (an f32 copy of the state carried
+ *                   between segments, so the state is rounded to bf16 once,
+ *                   at the end).  Below that: KDA_ERR_ARG.
+ *  passes           0: the library chooses (two passes while 2 * M * H is at
+ *                   most the compute-unit count of the stream's device, else
+ *                   the one-pass kernel of kda_prefill_gated, which then
+ *                   fills the device and leaves the workspace untouched);
+ *                   1: one pass (workspace unused, may be NULL, not
+ *                   checked); 2: two passes.  For 0 and 2 the workspace is
+ *                   checked (NULL, alignment, size, overlap) whichever form
+ *                   runs.
+ *
+ * Results agree with the token-by-token recurrence to the rounding of the
+ * reordered f32 arithmetic, as kda_prefill_gated's; the one- and two-pass
+ * forms perform the same operations per chunk and column in the same order
+ * but are not guaranteed bit-identical to each other.  Returns a KDA_* status.
+ */
+int kda_prefill_gated_ws(int L, int M, int H, int D, int state_dtype,
+                         void *state, const void *x_qkv, const void *conv_w,
+                         const void *conv_in, void *conv_out,
+                         const void *f_gate, const float *A_log,
+                         const float *dt_bias, const void *beta_logit,
+                         float gate_lower_bound, float scale, void *o,
+                         void *workspace, size_t workspace_bytes, int passes,
+                         void *stream);
 
 /*
  * kda_conv_step -- the conv stage alone, over C independent channels

@@ -26,7 +26,7 @@ def fake(i, misalign=0):
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|size_t|const char \*)\s*(\w+)\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -268,6 +268,42 @@ def test_prefill_errors(lib):
     assert call(ptrs=q) == binding.KDA_ERR_ALIAS
     q = list(p); q[0] = q[1] + 8192     # state inside x
     assert call(ptrs=q) == binding.KDA_ERR_ALIAS
+
+
+def test_prefill_workspace_errors(lib):
+    rec = 42496
+    assert lib.kda_prefill_workspace_bytes(32, 2, 64, 128) == 2 * 2 * 64 * rec
+    assert lib.kda_prefill_workspace_bytes(33, 1, 1, 128) == 3 * rec
+    assert lib.kda_prefill_workspace_bytes(0, 1, 1, 128) == 0
+    assert lib.kda_prefill_workspace_bytes(16, 1, 1, 64) == 0
+    assert lib.kda_prefill_workspace_bytes(16, 0, 1, 128) == 0
+    assert lib.kda_prefill_workspace_bytes(1 << 30, 1 << 12, 64, 128) == 0     # above 2^40
+    p = [fake(i) for i in range(11)]     # ... as test_prefill_errors, then the workspace
+
+    def call(L=32, M=1, H=64, D=128, sdt=0, ptrs=p, wsb=None, passes=0, lb=-5.0):
+        s, x, w, ci, co, f, A, b, bl, o, ws = ptrs
+        if wsb is None:
+            wsb = lib.kda_prefill_workspace_bytes(L, M, H, D)
+        return lib.kda_prefill_gated_ws(L, M, H, D, sdt, s, x, w, ci, co, f, A, b, bl, lb, 0.125, o, ws, wsb,
+                                         passes, None)
+    for ps in (-1, 3):
+        assert call(passes=ps) == binding.KDA_ERR_ARG
+    assert call(D=64) == binding.KDA_ERR_SHAPE
+    assert call(lb=-6.0) == binding.KDA_ERR_ARG
+    assert call(L=0, ptrs=[None] * 11) == binding.KDA_OK
+    for ps in (0, 2):
+        q = list(p); q[10] = None
+        assert call(ptrs=q, passes=ps) == binding.KDA_ERR_NULL
+        q = list(p); q[10] += 8
+        assert call(ptrs=q, passes=ps) == binding.KDA_ERR_ALIGN
+        # below one chunk's records for every head
+        assert call(wsb=64 * rec - 16, passes=ps) == binding.KDA_ERR_ARG
+        # bf16 state with a partial workspace also needs the f32 stage
+        assert call(sdt=1, wsb=64 * rec, passes=ps) == binding.KDA_ERR_ARG
+        q = list(p); q[10] = q[1] + 4096    # workspace inside x
+        assert call(ptrs=q, passes=ps) == binding.KDA_ERR_ALIAS
+        q = list(p); q[10] = q[0] - 4096    # workspace running into the state
+        assert call(ptrs=q, passes=ps) == binding.KDA_ERR_ALIAS
 
 
 def test_binding_rejects_host_tensors():
