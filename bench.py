@@ -11,7 +11,7 @@ q/k/v, alpha, beta per step) rotate across steps.
 Headline: M = 32 streams, FP32 state.  Also measured (``secondary``): M = 8
 with FP32 and BF16 state, M = 128 with BF16 state, M = 1, the gated and
 layer steps, T = 8 tokens per call, and the chunked prefill (tokens/s and
-FP32 matrix-core TFLOP/s for M streams x L tokens of one layer).
+FP32-equivalent TFLOP/s for M streams x L tokens of one layer).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -55,11 +55,18 @@ SIDE_BYTES = {"plain": (393_472, 196_608), "gated": (376_960, 196_608 + 32_768 +
 MULTI_TOKEN_BYTES, MULTI_CALL_BYTES = 98_560, 294_912
 MULTI_T = 8
 CONV_W_BYTES = 196_608
-# chunked prefill (16-token chunks, D = 128), per (chunk, head): the
-# intra-chunk products A and P 2 x 2 C^2 D, the UT products W = M (Gamma K)
-# and U = M V 2 x 2 C^2 D, the state products W S and (Gamma Q) S
-# 2 x 2 C D^2, P Delta 2 C^2 D, the state update 2 C D^2 -> 1,900,544 flops
-PREFILL_FLOPS_PER_CHUNK_HEAD = 1_900_544
+# chunked prefill (16-token chunks, D = 128), per (chunk, head), as the chunk
+# form is computed: the intra-chunk products A and P 2 x 2 C^2 D, the
+# triangular solves for W and U by substitution 2 x 2 (C (C - 1) / 2) D, the
+# state products W S and (Gamma Q) S 2 x 2 C D^2, P Delta 2 C^2 D, the state
+# update 2 C D^2 -> 1,830,912 flops (FP32-equivalent: each is computed to
+# FP32 accuracy)
+PREFILL_FLOPS_PER_CHUNK_HEAD = 1_830_912
+# bf16 matrix-core flops the kernels issue for the three state products,
+# per (chunk, head): W S and the update from three-way splits with six piece
+# products each, (Gamma Q) S with three -> (6 + 3 + 6) x 2 C D^2
+PREFILL_BF16_MFMA_FLOPS_PER_CHUNK_HEAD = 15 * 2 * 16 * 128 * 128
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix
 PREFILL_CHUNK = 16
 # per stream and token: x 49,152 + f 16,384 + beta logit 128 + o 16,384 read or
 # written; per stream the conv state 294,912; per layer conv w, dt_bias, A_log
@@ -68,7 +75,8 @@ PREFILL_LAYER_BYTES = 196_608 + 32_768 + 256
 MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X dense FP32 matrix
 # (streams, tokens per stream, state dtype) of the prefill lines; the last two are
 # the T-token shapes of kda_decode_multi, for the chunked path
-PREFILL_SHAPES = ((8, 2048, "f32"), (1, 8192, "f32"), (32, 1024, "bf16"), (32, 8, "f32"), (32, 16, "f32"))
+PREFILL_SHAPES = ((8, 2048, "f32"), (1, 8192, "f32"), (2, 4096, "f32"), (1, 4096, "bf16"), (32, 1024, "bf16"),
+                  (32, 8, "f32"), (32, 16, "f32"))
 
 
 def log(msg):
@@ -337,8 +345,11 @@ def measure(wl, state_dtype, steps, warmup, n_inputs, mode="plain", T=1, check=F
 
 
 def measure_prefill(M, L, state_dtype, steps, warmup, H=64, D=128):
-    """kda_prefill_gated over M streams x L tokens of one layer, launched
-    `steps` times on the same buffers (state and conv state carried along)."""
+    """kda_prefill_gated_ws over M streams x L tokens of one layer, launched
+    `steps` times on the same buffers (state and conv state carried along):
+    while 2 M H is at most the CU count the library chooses (passes = 0: two
+    passes) over a one-segment workspace allocated before timing, else the
+    one-pass form is asked for (passes = 1, no workspace)."""
     import torch
 
     import kda_synth
@@ -349,25 +360,28 @@ def measure_prefill(M, L, state_dtype, steps, warmup, H=64, D=128):
     gp = kda_synth.gate_params(wl, 0, "cuda:0")
     seq = kda_synth.sequence_inputs(wl, 0, L, "cuda:0")
     o = torch.empty((M, L, H, D), dtype=torch.bfloat16, device="cuda:0")
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    two = 2 * M * H <= ncu
+    wsb = lib.kda_prefill_workspace_bytes(L, M, H, D) if two else 16
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
     torch.cuda.synchronize()
     vp = ctypes.c_void_p
     sdt = kda.KDA_STATE_F32 if state_dtype == "f32" else kda.KDA_STATE_BF16
     stream = torch.cuda.Stream()
-    # the conv state alternates between two buffers (conv_in != conv_out):
-    # with few heads the library then splits each head over two workgroups
+    # the conv state alternates between two buffers (conv_in != conv_out)
     cs = (li["conv_state"], li["conv_state"].clone())
     args = [(L, M, H, D, sdt, vp(li["state"].data_ptr()), vp(seq["x"].data_ptr()),
              vp(li["conv_w"].data_ptr()), vp(cs[i].data_ptr()), vp(cs[1 - i].data_ptr()),
              vp(seq["f"].data_ptr()), vp(gp["A_log"].data_ptr()), vp(gp["dt_bias"].data_ptr()),
              vp(seq["beta_logit"].data_ptr()), ctypes.c_float(-5.0), ctypes.c_float(wl.scale),
-             vp(o.data_ptr()), vp(stream.cuda_stream)) for i in (0, 1)]
+             vp(o.data_ptr()), vp(ws.data_ptr()), wsb, 0 if two else 1, vp(stream.cuda_stream)) for i in (0, 1)]
     calls = [0]
 
     def launch():
-        rc = lib.kda_prefill_gated(*args[calls[0] & 1])
+        rc = lib.kda_prefill_gated_ws(*args[calls[0] & 1])
         calls[0] += 1
         if rc:
-            raise RuntimeError(f"kda_prefill_gated returned {rc}")
+            raise RuntimeError(f"kda_prefill_gated_ws returned {rc}")
 
     with torch.cuda.stream(stream):
         for _ in range(warmup):
@@ -382,16 +396,26 @@ def measure_prefill(M, L, state_dtype, steps, warmup, H=64, D=128):
     sec = s.elapsed_time(e) / 1e3 / steps
     # per token (a ragged last chunk counts its tokens, not the padded 16)
     flops = PREFILL_FLOPS_PER_CHUNK_HEAD * M * H * L // PREFILL_CHUNK
+    bf16_flops = PREFILL_BF16_MFMA_FLOPS_PER_CHUNK_HEAD * M * H * ((L + PREFILL_CHUNK - 1) // PREFILL_CHUNK)
     nbytes = (M * (L * PREFILL_TOKEN_BYTES + PREFILL_STREAM_BYTES) + PREFILL_LAYER_BYTES
               + 2 * wl.state_bytes(state_dtype))
-    del li, gp, seq, o, cs
+    if two:
+        nbytes += 2 * wsb          # pass 1 writes every chunk's record, pass 2 reads it
+    del li, gp, seq, o, cs, ws
     torch.cuda.empty_cache()
     return {"workload": f"prefill_m{M}_l{L}", "M": M, "L": L, "H": H, "D": D,
-            "state_dtype": state_dtype, "entry_point": "kda_prefill_gated", "launch": "eager",
+            "state_dtype": state_dtype, "entry_point": "kda_prefill_gated_ws",
+            "form": "two-pass" if two else "one-pass", "workspace_bytes": wsb if two else 0, "launch": "eager",
             "ms_per_layer": sec * 1e3, "tokens_per_s_per_layer": M * L / sec,
             "us_per_token_layer": sec * 1e6 / (M * L),
-            "roofline": {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_F32_PEAK_TFLOPS,
+            "roofline": {"bound": "alu", "achieved": flops / sec / 1e12, "peak": MFMA_F32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": flops / sec / 1e12 / MFMA_F32_PEAK_TFLOPS,
+                         "achieved_is": "FP32-equivalent flops of the chunk form as computed (W and U by "
+                                        "substitution) over time, against MI355X's FP32 peak",
+                         "limiter": ("pass 2's per-chunk dependency chain (one chunk at a time per head)"
+                                     if two else "VALU issue and LDS/barrier latency (counters in profiles/)"),
+                         "bf16_mfma_TFLOPs_executed": bf16_flops / sec / 1e12,
+                         "bf16_mfma_frac": bf16_flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                          "flops_per_launch": flops, "alg_bytes_per_launch": nbytes,
                          "alg_GBps": nbytes / sec / 1e9}}
 
@@ -651,9 +675,10 @@ def main():
         for M, L, sdt in PREFILL_SHAPES:
             r = measure_prefill(M, L, sdt, max(5, args.steps // 20), 2)
             secondary.append(r)
-            log(f"  {r['workload']} {sdt}: {r['ms_per_layer']:.3f} ms/layer, {r['us_per_token_layer'] * 1e3:.1f} "
-                f"ns/token-layer, {r['roofline']['achieved']:.1f} TFLOP/s ({100 * r['roofline']['frac']:.1f}% "
-                f"of FP32 MFMA), {r['roofline']['alg_GBps']:.0f} GB/s")
+            log(f"  {r['workload']} {sdt} ({r['form']}): {r['ms_per_layer']:.3f} ms/layer, "
+                f"{r['us_per_token_layer'] * 1e3:.1f} ns/token-layer, {r['roofline']['achieved']:.1f} FP32-equivalent "
+                f"TFLOP/s ({100 * r['roofline']['frac']:.1f}% of FP32 peak), bf16 MFMA "
+                f"{100 * r['roofline']['bf16_mfma_frac']:.1f}% of peak, {r['roofline']['alg_GBps']:.0f} GB/s")
 
     ceiling = None
     if not args.no_ceiling:

@@ -117,9 +117,12 @@ def test_prefill_empty():
     assert torch.equal(S, li["state"])
 
 
-# The benchmark's prefill shapes, inputs and launch (bench.py's measure_prefill:
-# workload name prefill_m{M}_l{L}, seed 7, whole-sequence draws, lower bound -5),
-# checked on sampled (stream, head) units over every token of the sequence.
+# The one-pass kernel at the benchmark's prefill shapes and inputs (bench.py's
+# measure_prefill: workload name prefill_m{M}_l{L}, seed 7, whole-sequence
+# draws, lower bound -5, conv state ping-pong), checked on sampled (stream,
+# head) units over every token of the sequence.  The benchmark launches the
+# shapes with 2 M H above the CU count in this form; the others run two
+# passes there (tests/test_prefill_ws_gpu.py).
 BENCH_SHAPES = [(8, 2048, "f32"), (32, 1024, "bf16"), (1, 8192, "f32"), (32, 8, "f32"), (32, 16, "f32")]
 
 
