@@ -399,6 +399,40 @@ int kda_prefill_gated_ws(int L, int M, int H, int D, int state_dtype, void* stat
     return map_hip(kda::launch_prefill_ws(a, workspace, workspace_bytes, ncu));
 }
 
+int kda_prefill_gated_noalloc(int L, int M, int H, int D, int state_dtype, void* state, const void* x_qkv,
+                              const void* conv_w, const void* conv_in, void* conv_out, const void* f_gate,
+                              const float* A_log, const float* dt_bias, const void* beta_logit,
+                              float gate_lower_bound, float scale, void* o, void* stream) {
+    kda::StepArgs a;
+    Range all[10];
+    const int rc = check_prefill(L, M, H, D, state_dtype, state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log,
+                                 dt_bias, beta_logit, gate_lower_bound, scale, o, stream, &a, all);
+    if (rc == -1) return KDA_OK;
+    if (rc != KDA_OK) return rc;
+    const long units = (long)M * H;
+    const int ncu = stream_cus(stream);
+    if (units * 2 > ncu) return map_hip(kda::launch_prefill(a));     // one pass: no scratch
+    // two passes through the device's scratch array: it must hold one
+    // chunk's records for every (stream, head), and for bf16 state with more
+    // than one segment also the f32 stage
+    const size_t cap = kda::prefill_scratch_bytes();
+    const size_t full = kda_prefill_workspace_bytes(L, M, H, D);
+    size_t need = (size_t)units * kda::prefill_record_bytes();
+    if (state_dtype == KDA_STATE_BF16 && full > cap) need += kda::prefill_state_stage_bytes(M, H);
+    if (full == 0 || need > cap) return KDA_ERR_ARG;
+    int dev = 0;
+    if (stream) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice((hipStream_t)stream, &d) != hipSuccess) return KDA_ERR_HIP;
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return KDA_ERR_HIP;
+    }
+    void* ws = nullptr;
+    if (kda::prefill_scratch_address(dev, &ws) != hipSuccess) return KDA_ERR_HIP;
+    return map_hip(kda::launch_prefill_ws(a, ws, cap, ncu));
+}
+
 int kda_conv_step(int M, int C, const void* x, const void* conv_w, const void* conv_in,
                   void* conv_out, float* y, void* stream) {
     if (M < 0 || C < 1 || (C % 8) != 0) return KDA_ERR_ARG;
@@ -455,7 +489,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_DTYPE: return "unknown state dtype";
     case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KDA_ERR_ALIAS: return "an output overlaps an input";
-    case KDA_ERR_ARG: return "invalid argument (negative size, non-finite scale, bad gate or norm parameter, overflow)";
+    case KDA_ERR_ARG: return "invalid argument (negative size, non-finite scale, bad gate or norm parameter, overflow, workspace too small)";
     case KDA_ERR_HIP: return "the HIP runtime refused the launch";
     default: return "unknown status";
     }

@@ -49,6 +49,10 @@ hipError_t launch_prefill_ws(const StepArgs& a, void* ws, size_t ws_bytes, int n
 size_t prefill_record_bytes();
 // f32 copy of the state kept between segments for bf16 storage
 size_t prefill_state_stage_bytes(int M, int H);
+// size of the allocation-free entry point's per-device scratch array, and
+// its device address on device `dev` (looked up on the first call per device)
+size_t prefill_scratch_bytes();
+hipError_t prefill_scratch_address(int dev, void** out);
 hipError_t launch_conv_step(int M, int C, const void* x, const void* w, const void* cin,
                             void* cout, float* y, void* stream);
 

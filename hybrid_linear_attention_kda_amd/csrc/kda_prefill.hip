@@ -61,6 +61,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -1200,6 +1202,45 @@ hipError_t launch_prefill_ws(const StepArgs& a, void* ws, size_t ws_bytes, int n
             e = launch_scan<float, float>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
         if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch memory of the allocation-free entry point: the two-pass form's
+// workspace as a file-scope device array, one copy per GPU the library runs
+// on, held until the process ends.  Host code never passes `scratch` itself
+// (its host-side name is not a device address): the device address is
+// looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept.
+namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+size_t prefill_scratch_bytes() { return kScratchBytes; }
+
+hipError_t prefill_scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return hipSuccess;
 }
 

@@ -25,7 +25,7 @@ KDA_GATE_BOUNDED, KDA_GATE_SOFTPLUS = 0, 1
 #: every symbol ``include/kda.h`` declares
 EXPORTS = ("kda_decode_step", "kda_decode_step_split", "kda_decode_step_gated",
            "kda_decode_layer_step", "kda_decode_multi", "kda_prefill_gated", "kda_prefill_gated_ws",
-           "kda_prefill_workspace_bytes", "kda_conv_step",
+           "kda_prefill_gated_noalloc", "kda_prefill_workspace_bytes", "kda_conv_step",
            "kda_recurrent_step", "kda_status_string", "kda_version")
 
 
@@ -64,6 +64,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill_gated_ws.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, fp, fp, vp, f, f, vp, vp,
                                          ctypes.c_size_t, i, vp]
     lib.kda_prefill_gated_ws.restype = i
+    lib.kda_prefill_gated_noalloc.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, fp, fp, vp, f, f, vp, vp]
+    lib.kda_prefill_gated_noalloc.restype = i
     lib.kda_prefill_workspace_bytes.argtypes = [i, i, i, i]
     lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_conv_step.argtypes = [i, i, vp, vp, vp, vp, fp, vp]
@@ -290,7 +292,7 @@ def kda_prefill_gated(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt
     dt_bias [H*D] f32, beta_logit [M,L,H] bf16, o [M,L,H,D] bf16; D = 128.
     With ``workspace`` (a contiguous GPU tensor of any dtype) the call goes to
     ``kda_prefill_gated_ws`` with ``passes`` (0 choose, 1 one pass, 2 two
-    passes)."""
+    passes); with ``workspace="noalloc"`` to ``kda_prefill_gated_noalloc``."""
     lib = load()
     if state.dim() != 4 or x_qkv.dim() != 4:
         raise ValueError("state must be [M, H, D, D] and x_qkv [M, L, 3, H*D]")
@@ -315,6 +317,15 @@ def kda_prefill_gated(state, x_qkv, conv_w, conv_in, conv_out, f_gate, A_log, dt
                                      _p(conv_in), _p(conv_out), _p(f_gate), _p(A_log), _p(dt_bias),
                                      _p(beta_logit), float(lower_bound), float(scale), _p(o),
                                      _stream(dev, stream)))
+        return
+    if isinstance(workspace, str):
+        if workspace != "noalloc":
+            raise ValueError("workspace must be a tensor or 'noalloc'")
+        _check("kda_prefill_gated_noalloc",
+               lib.kda_prefill_gated_noalloc(L, M, H, D, _state_code(state), _p(state), _p(x_qkv), _p(conv_w),
+                                             _p(conv_in), _p(conv_out), _p(f_gate), _p(A_log), _p(dt_bias),
+                                             _p(beta_logit), float(lower_bound), float(scale), _p(o),
+                                             _stream(dev, stream)))
         return
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the state's device")

@@ -315,6 +315,35 @@ int kda_prefill_gated_ws(int L, int M, int H, int D, int state_dtype,
                          void *stream);
 
 /*
+ * kda_prefill_gated_noalloc -- kda_prefill_gated_ws for callers that cannot
+ * allocate device memory or own a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the two-pass
+ * form's workspace is a 64 MiB array in the library's device memory, one
+ * per GPU, held until the process ends.  The call itself allocates nothing
+ * (no hipMalloc / hipFree / allocating library routine).
+ *
+ *  Arguments, layouts, ranges and aliasing rules as kda_prefill_gated.  The
+ *  form is chosen as kda_prefill_gated_ws with passes = 0; the two passes
+ *  run in segments of as many chunks as the array holds records for.
+ *  Above the array's capacity (M * H * KDA_PREFILL_RECORD_BYTES, plus
+ *  M * H * 65536 for bf16 state when the sequence takes more than one
+ *  segment, over 64 MiB -- only reachable where 2 * M * H is at most the
+ *  device's CU count, i.e. on devices of more than ~3000 CUs): KDA_ERR_ARG.
+ *  The array keeps whatever the last call left; nothing in it needs to
+ *  start at any value.  Calls on one GPU share its array: calls that may
+ *  overlap in time on one GPU (different streams) race and must not be made.
+ *  On the first call on a device the library looks up the array's device
+ *  address (KDA_ERR_HIP if the runtime cannot).  Returns a KDA_* status.
+ */
+int kda_prefill_gated_noalloc(int L, int M, int H, int D, int state_dtype,
+                              void *state, const void *x_qkv, const void *conv_w,
+                              const void *conv_in, void *conv_out,
+                              const void *f_gate, const float *A_log,
+                              const float *dt_bias, const void *beta_logit,
+                              float gate_lower_bound, float scale, void *o,
+                              void *stream);
+
+/*
  * kda_conv_step -- the conv stage alone, over C independent channels
  * ("GLM-5.3 deep dive", 8.2.4 step 2; one launch over all q|k|v channels).
  *

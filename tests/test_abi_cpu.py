@@ -306,6 +306,29 @@ def test_prefill_workspace_errors(lib):
         assert call(ptrs=q, passes=ps) == binding.KDA_ERR_ALIAS
 
 
+def test_prefill_noalloc_errors(lib):
+    """The allocation-free prefill validates like kda_prefill_gated before
+    any HIP call (fake pointers, never dereferenced)."""
+    p = [fake(i) for i in range(10)]
+
+    def call(L=32, M=1, H=64, D=128, sdt=0, ptrs=p, lb=-5.0, scale=0.125):
+        s, x, w, ci, co, f, A, b, bl, o = ptrs
+        return lib.kda_prefill_gated_noalloc(L, M, H, D, sdt, s, x, w, ci, co, f, A, b, bl, lb, scale, o, None)
+    assert call(L=-1) == binding.KDA_ERR_ARG
+    assert call(D=64) == binding.KDA_ERR_SHAPE
+    assert call(sdt=2) == binding.KDA_ERR_DTYPE
+    assert call(lb=0.0) == binding.KDA_ERR_ARG
+    assert call(scale=math.inf) == binding.KDA_ERR_ARG
+    assert call(L=0, ptrs=[None] * 10) == binding.KDA_OK
+    for i in range(10):
+        q = list(p); q[i] = None
+        assert call(ptrs=q) == binding.KDA_ERR_NULL
+        q = list(p); q[i] += 4
+        assert call(ptrs=q) == binding.KDA_ERR_ALIGN
+    q = list(p); q[9] = q[1]            # o over x
+    assert call(ptrs=q) == binding.KDA_ERR_ALIAS
+
+
 def test_binding_rejects_host_tensors():
     M, H, D = 1, 2, 16
     st = torch.zeros(M, H, D, D)
