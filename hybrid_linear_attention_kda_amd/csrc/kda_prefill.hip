@@ -886,42 +886,56 @@ void prep_kernel(const Ptrs p, const int L, const int M, const int c0, const int
     }
 }
 
-// Pass 2: per workgroup TPW column tiles of head (m, h), two waves per tile,
+// Pass 2: per workgroup TPW column tiles of head (m, h), KS waves per tile,
 // for chunks [c0, c0 + nch).  Tile ct = TPW * split + i covers value columns
-// [16 ct, 16 ct + 16); its two waves split the key rows: wave half hs holds
-// rows [64 hs, 64 hs + 64) of the tile (state blocks kb = 2 hs, 2 hs + 1) in
-// the D layout of the 16 x 16 MFMAs -- lane (l16, g4) holds rows
-// 16 mt + 4 g4 + r, mt = 4 hs .. 4 hs + 3, of column 16 ct + l16.  Per chunk
-// each wave forms its rows' share of W S (the half-0 wave starting from U)
-// and of (Gamma . Q) S; the two shares meet in LDS after a barrier and both
-// waves add them in the same order, so both hold the same Delta; the half-0
-// wave writes the outputs, and each wave updates its own rows.
-// The shared part of each chunk's record is staged in LDS, double-buffered:
-// a chunk's part is fetched into registers two chunks ahead and written to
-// the other buffer at the end of the chunk before it (two barriers per
-// chunk).
-// The state comes from `sin` and goes to `sout`: the caller's state (type
-// TS) at the ends of the call, f32 in the workspace between segments.
-template <int TPW>
+// [16 ct, 16 ct + 16); its KS waves split the key rows: wave ks of the tile
+// holds rows [128 ks / KS, 128 (ks + 1) / KS) (state blocks kb of 32 rows,
+// KB = 4 / KS of them) in the D layout of the 16 x 16 MFMAs -- lane (l16, g4)
+// holds rows 16 mt + 4 g4 + r of column 16 ct + l16.  Per chunk each wave
+// forms its rows' share of W S (wave 0 of the tile starting from U) and of
+// (Gamma . Q) S; the shares meet in LDS after a barrier and every wave of the
+// tile adds them in the same order, so all hold the same Delta; each wave
+// writes the outputs of 4 / KS of a lane's four tokens and updates its own
+// rows.  The shared part of each chunk's record is staged in LDS,
+// double-buffered: a chunk's part is fetched into registers two chunks ahead
+// and written to the other buffer at the end of the chunk before it (two
+// barriers per chunk).  The state comes from `sin` and goes to `sout`: the
+// caller's state (type TS) at the ends of the call, f32 in the workspace
+// between segments.
+template <int TPW, int KS>
 struct ScanSmem {
-    // the shared record part, rounded up to whole staging rounds of the
-    // workgroup's threads (the extra units are the start of the U tiles,
-    // inside the record, and are not read from LDS)
-    u32x4 rec[2][(R_SHARED + TPW * 128 - 1) / (TPW * 128) * (TPW * 128)];
-    f32x4 part[2 * TPW][2][64];        // [wave][W S share, (Gamma . Q) S share][lane]
-    u32x4 dp[2 * TPW][3][2][16];       // Delta pieces [wave][piece][token half][column]
+    // the shared record part, then the U tiles of the workgroup's TPW
+    // column tiles, rounded up to whole staging rounds of its threads (the
+    // units past them repeat the record's first ones and are not read)
+    u32x4 rec[2][(R_SHARED + TPW * 64 + TPW * KS * 64 - 1) / (TPW * KS * 64) * (TPW * KS * 64)];
+    f32x4 part[TPW * KS][2][64];       // [wave][W S share, (Gamma . Q) S share][lane]
+    u32x4 dp[TPW * KS][3][2][16];      // Delta pieces [wave][piece][token half][column]
 };
 
-template <typename TSI, typename TSO, int TPW>
-__global__ __launch_bounds__(TPW * 128)
+// the sum of the KS shares of one tile's waves w0 .. w0 + KS - 1, as a
+// balanced tree (the same order in every wave)
+template <int KS>
+__device__ __forceinline__ f32x4 sum_shares(const f32x4 (*part)[2][64], int w0, int which, int lane) {
+    if constexpr (KS == 2) {
+        return part[w0][which][lane] + part[w0 + 1][which][lane];
+    } else {
+        return (part[w0][which][lane] + part[w0 + 1][which][lane]) +
+               (part[w0 + 2][which][lane] + part[w0 + 3][which][lane]);
+    }
+}
+
+template <typename TSI, typename TSO, int TPW, int KS>
+__global__ __launch_bounds__(TPW * KS * 64)
 void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int nch,
                  const u32x4* __restrict__ ws, const TSI* sin, TSO* sout, const int write_conv)
 {
+    static_assert(KS == 2 || KS == 4, "two or four waves per tile");
+    constexpr int KB = 4 / KS;                         // 32-row state blocks per wave
     constexpr int NS = 8 / TPW;                        // workgroups per head
-    constexpr int NT = TPW * 128;
-    constexpr int PER = (R_SHARED + NT - 1) / NT;      // 16-byte units each thread stages
-    static_assert(PER * NT <= R_SIZE, "staging stays inside the record");
-    __shared__ ScanSmem<TPW> sm;
+    constexpr int NT = TPW * KS * 64;
+    constexpr int STAGED = R_SHARED + TPW * 64;        // shared part + this workgroup's U tiles
+    constexpr int PER = (STAGED + NT - 1) / NT;        // 16-byte units each thread stages
+    __shared__ ScanSmem<TPW, KS> sm;
     // XCD-aware: workgroups go to the 8 XCDs round robin; the NS workgroups of
     // a head sit on one XCD, so they read its records through one L2
     const int units = M * p.H;
@@ -942,64 +956,82 @@ void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int
     const int m = unit / p.H, h = unit - m * p.H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hs = wv & 1, ti = wv >> 1;
+    const int ks = wv % KS, ti = wv / KS, w0 = wv - ks;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int ct = TPW * split + ti, col = 16 * ct + l16;
     const size_t rstride = (size_t)M * p.H * R_SIZE;   // from one chunk's records to the next
     const u32x4* const rec0 = ws + (size_t)unit * R_SIZE;
 
-    float S[4][4];
+    float S[2 * KB][4];
     {
         const TSI* const st = sin + (size_t)unit * PD * PD;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 2 * KB; ++mi)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[mi][r] = load_state_elem(st + (size_t)(16 * (4 * hs + mi) + 4 * g4 + r) * PD + col);
+                S[mi][r] = load_state_elem(st + (size_t)(16 * (2 * KB * ks + mi) + 4 * g4 + r) * PD + col);
     }
 
     // Records are fetched two chunks ahead (their latency from HBM exceeds
     // a chunk's work): register set 0 holds even chunks, set 1 odd ones,
     // and the loop runs two chunks per iteration so that both sets stay
-    // compile-time arrays.
-    u32x4 stg0[PER], stg1[PER];
-    f32x4 un0 = f32x4{0.f, 0.f, 0.f, 0.f}, un1 = un0;
-    auto fetch = [&](u32x4 (&stg)[PER], f32x4& un, int c) {
-        const u32x4* const rc = rec0 + (size_t)c * rstride;
+    // compile-time arrays.  Every thread issues the same loads on every
+    // chunk (the index clamped to the last chunk, so the last two chunks
+    // load a record again, unused), and they are consumed only by the
+    // staging stores: with conditional loads, or loads consumed elsewhere,
+    // the compiler cannot count the loads issued after a set's and waits for
+    // all of them.  Unit e of the staged span is record unit e below
+    // R_SHARED, then the U tiles of this workgroup's column tiles, then
+    // repeats of the record's first units.
+    // The loads are raw buffer loads over one record: a wave-uniform
+    // descriptor per chunk and loop-invariant per-thread byte offsets, so no
+    // address register is rewritten per chunk (a rewritten address register
+    // that once held a load's result makes the compiler wait for loads
+    // still in flight).
+    int src[PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) stg[i] = rc[tid + i * NT];
-        if (hs == 0) un = __builtin_bit_cast(f32x4, rc[R_U + ct * 64 + lane]);
+    for (int i = 0; i < PER; ++i) {
+        const int e = tid + i * NT;
+        src[i] = 16 * (e < R_SHARED ? e : (e < STAGED ? R_U + TPW * split * 64 + (e - R_SHARED) : e - STAGED));
+    }
+    u32x4 stg0[PER], stg1[PER];
+    auto fetch = [&](u32x4 (&stg)[PER], int c) {
+        const auto rs = stream_rsrc(rec0 + (size_t)c * rstride, R_SIZE * 16);
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            stg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, src[i], 0, 0));
     };
     auto put = [&](const u32x4 (&stg)[PER], int buf) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) sm.rec[buf][tid + i * NT] = stg[i];
     };
 
-    // chunk c from LDS buffer c & 1 with U from `uc`; `nxt` (chunk c + 1's
-    // record, fetched a chunk ago) goes to the other buffer at the end, and
-    // `cur` (free once chunk c's record is in LDS) takes chunk c + 2's
-    auto chunk = [&](int c, u32x4 (&cur)[PER], f32x4& ucur, const u32x4 (&nxt)[PER]) {
+    // chunk c from LDS buffer c & 1; `nxt` (chunk c + 1's record, fetched a
+    // chunk ago) goes to the other buffer at the end, and `cur` (free once
+    // chunk c's record is in LDS) takes chunk c + 2's
+    auto chunk = [&](int c, u32x4 (&cur)[PER], const u32x4 (&nxt)[PER]) {
         const int buf = c & 1;
         const u32x4* const R = sm.rec[buf];
         const int t0 = (c0 + c) * PC;
-        const f32x4 uc = ucur;
-        if (c + 2 < nch) fetch(cur, ucur, c + 2);
+        fetch(cur, min(c + 2, nch - 1));
 
         // ---- 4. this wave's share of Delta = U - W S and of (Gamma . Q) S ----
-        u32x4 wp[2][3], gp[2][2];
+        u32x4 wp[KB][3], gp[KB][2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int kb = 2 * hs + i;
+        for (int i = 0; i < KB; ++i) {
+            const int kb = KB * ks + i;
 #pragma unroll
             for (int q = 0; q < 3; ++q) wp[i][q] = R[R_WP + (kb * 3 + q) * 64 + lane];
 #pragma unroll
             for (int q = 0; q < 2; ++q) gp[i][q] = R[R_GQ + (kb * 2 + q) * 64 + lane];
         }
-        f32x4 dk[2], ok = {0.f, 0.f, 0.f, 0.f};
-        dk[0] = uc;
-        dk[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 dk[KB], ok = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < KB; ++i)
+            dk[i] = (i == 0 && ks == 0) ? __builtin_bit_cast(f32x4, R[R_SHARED + ti * 64 + lane])
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
             u32x4 sb[3];
             split8(f32x4{S[2 * i][0], S[2 * i][1], S[2 * i][2], S[2 * i][3]},
                    f32x4{S[2 * i + 1][0], S[2 * i + 1][1], S[2 * i + 1][2], S[2 * i + 1][3]}, sb);
@@ -1011,11 +1043,11 @@ void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int
         }
         // the update's operands from the record, read before the barrier
         const int hh = g4 & 1, sel = g4 >> 1;
-        u32x4 ka[4][3];
-        f32x4 gm[4];
+        u32x4 ka[2 * KB][3];
+        f32x4 gm[2 * KB];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int mt = 4 * hs + mi;
+        for (int mi = 0; mi < 2 * KB; ++mi) {
+            const int mt = 2 * KB * ks + mi;
             gm[mi] = __builtin_bit_cast(f32x4, R[R_GM + 4 * mt + g4]);
 #pragma unroll
             for (int mm = 0; mm < 3; ++mm) {
@@ -1023,11 +1055,13 @@ void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int
                 ka[mi][mm] = R[R_KT + ((q * 8 + mt) * 2 + hh) * 16 + l16];
             }
         }
-        sm.part[wv][0][lane] = dk[0] + dk[1];
+        if constexpr (KB == 2)
+            sm.part[wv][0][lane] = dk[0] + dk[1];
+        else
+            sm.part[wv][0][lane] = dk[0];
         sm.part[wv][1][lane] = ok;
         lds_barrier();
-        // both waves of the tile add the two shares in the same order
-        const f32x4 dacc = sm.part[wv & ~1][0][lane] + sm.part[wv | 1][0][lane];
+        const f32x4 dacc = sum_shares<KS>(sm.part, w0, 0, lane);
         {
             uint32_t p0a, p1a, p2a, p0b, p1b, p2b;
             split2(dacc[0], dacc[1], p0a, p1a, p2a);
@@ -1040,13 +1074,13 @@ void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int
         }
         lds_wave_fence();
 
-        // ---- 5. S' = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta; O = (Gamma . Q) S + P Delta (half 0) ----
+        // ---- 5. S' = Diag(gamma_C) S + ((gamma_C / Gamma) . K)^T Delta; O = (Gamma . Q) S + P Delta ----
         {
             u32x4 db[3];
 #pragma unroll
             for (int mm = 0; mm < 3; ++mm) db[mm] = sm.dp[wv][sel ? PAIR_B[2 * mm + 1] : PAIR_B[2 * mm]][hh][l16];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
+            for (int mi = 0; mi < 2 * KB; ++mi) {
                 f32x4 acc = {S[mi][0] * gm[mi].x, S[mi][1] * gm[mi].y, S[mi][2] * gm[mi].z, S[mi][3] * gm[mi].w};
 #pragma unroll
                 for (int mm = 0; mm < 3; ++mm) acc = mfma_bf16(ka[mi][mm], db[mm], acc);
@@ -1055,19 +1089,26 @@ void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int
             }
         }
         {
-            // both waves form the tile's outputs; each stores two of a lane's
-            // four tokens
-            f32x4 oacc = sm.part[wv & ~1][1][lane] + sm.part[wv | 1][1][lane];
+            // every wave of the tile forms the tile's outputs; each stores
+            // 4 / KS of a lane's four tokens
+            f32x4 oacc = sum_shares<KS>(sm.part, w0, 1, lane);
             const f32x4 p4 = __builtin_bit_cast(f32x4, R[R_P + lane]);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) oacc = mfma16(p4[kk], dacc[kk], oacc);
-            uint16_t* const ob = p.o + (((size_t)m * L + t0) * p.H + h) * PD + col;
-            const size_t ts = (size_t)p.H * PD;
+            // a buffer store over this chunk's valid tokens: the hardware
+            // drops the stores of tokens past the end of the sequence, so the
+            // store is unconditional and the compiler counts it exactly when
+            // it waits for the staged loads issued before it
+            const int nvalid = min(PC, L - t0);
+            const auto orsrc = stream_rsrc(p.o + (((size_t)m * L + t0) * p.H + h) * PD,
+                                           nvalid * p.H * PD * (int)sizeof(uint16_t));
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int t = 4 * g4 + 2 * hs + rr;
-                const float v = hs ? oacc[2 + rr] : oacc[rr];
-                if (t0 + t < L) ob[(size_t)t * ts] = (uint16_t)(cvt_pk_bf16(v, 0.0f) & 0xffffu);
+            for (int rr = 0; rr < 4 / KS; ++rr) {
+                const int r = (4 / KS) * ks + rr;
+                const int t = 4 * g4 + r;
+                const float v = r == 0 ? oacc[0] : (r == 1 ? oacc[1] : (r == 2 ? oacc[2] : oacc[3]));
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(cvt_pk_bf16(v, 0.0f) & 0xffffu), orsrc,
+                                                      (t * p.H * PD + col) * (int)sizeof(uint16_t), 0, 0);
             }
         }
         // the next chunk's shared record part into the other buffer; the
@@ -1076,21 +1117,21 @@ void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int
         lds_barrier();
     };
 
-    fetch(stg0, un0, 0);
-    if (nch > 1) fetch(stg1, un1, 1);
+    fetch(stg0, 0);
+    fetch(stg1, min(1, nch - 1));
     put(stg0, 0);
     lds_barrier();
     for (int c = 0; c < nch; c += 2) {
-        chunk(c, stg0, un0, stg1);
-        if (c + 1 < nch) chunk(c + 1, stg1, un1, stg0);
+        chunk(c, stg0, stg1);
+        if (c + 1 < nch) chunk(c + 1, stg1, stg0);
     }
 
     {
-        int so = (64 * hs + 4 * g4) * PD + col;
+        int so = (128 / KS * ks + 4 * g4) * PD + col;
         asm volatile("" : "+v"(so));
         TSO* const st = sout + (size_t)unit * PD * PD + so;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 2 * KB; ++mi)
 #pragma unroll
             for (int r = 0; r < 4; ++r) store_state_elem(st + (16 * mi + r) * PD, S[mi][r]);
     }
@@ -1128,15 +1169,15 @@ void scan_kernel(const Ptrs p, const int L, const int M, const int c0, const int
 // workspace after the records for bf16 storage (so bf16 state is rounded
 // once, at the end of the call, however many segments run).
 template <typename TSI, typename TSO>
-static hipError_t launch_scan(int tpw, const Ptrs& p, int L, int M, int c0, int nch, const u32x4* ws,
+static hipError_t launch_scan(int tpw, int ks, const Ptrs& p, int L, int M, int c0, int nch, const u32x4* ws,
                               const void* sin, void* sout, int write_conv, int units, hipStream_t stream) {
     const TSI* si = static_cast<const TSI*>(sin);
     TSO* so = static_cast<TSO*>(sout);
     void* args[] = {(void*)&p, (void*)&L, (void*)&M, (void*)&c0, (void*)&nch, (void*)&ws, (void*)&si, (void*)&so,
                     (void*)&write_conv};
-    const void* fn = tpw == 2 ? reinterpret_cast<const void*>(&scan_kernel<TSI, TSO, 2>)
-                              : reinterpret_cast<const void*>(&scan_kernel<TSI, TSO, 4>);
-    return hipLaunchKernel(fn, dim3((unsigned)(units * (8 / tpw))), dim3(tpw * 128), args, 0, stream);
+    const void* fn = tpw == 4 ? reinterpret_cast<const void*>(&scan_kernel<TSI, TSO, 4, 2>)
+                              : reinterpret_cast<const void*>(&scan_kernel<TSI, TSO, 2, 4>);
+    return hipLaunchKernel(fn, dim3((unsigned)(units * (8 / tpw))), dim3(tpw * ks * 64), args, 0, stream);
 }
 
 size_t prefill_state_stage_bytes(int M, int H) { return (size_t)M * H * PD * PD * sizeof(float); }
@@ -1162,11 +1203,12 @@ hipError_t launch_prefill_ws(const StepArgs& a, void* ws, size_t ws_bytes, int n
     u32x4* const rec = static_cast<u32x4*>(ws);
     float* const stage = bf16 ? reinterpret_cast<float*>(static_cast<char*>(ws) + (size_t)seg_chunks * per_chunk)
                               : static_cast<float*>(a.state);
-    // column tiles per pass-2 workgroup: 2 (one workgroup of 4 waves, one
-    // per SIMD, on each CU) while that gives at most a workgroup per CU,
-    // else 4 (8 waves; their registers allow one workgroup per CU)
+    // pass-2 workgroups: 2 column tiles of 4 waves each (one 32-row state
+    // block per wave; 8 waves) while that gives at most one workgroup per
+    // CU, else 4 tiles of 2 waves (8 waves; LDS allows one workgroup per CU)
     const long want = ncu > 0 ? ncu : 256;
     const int tpw = (long)units * 4 <= want ? 2 : 4;
+    const int ks = tpw == 4 ? 2 : 4;
     const hipStream_t stream = (hipStream_t)a.stream;
     for (int sgi = 0; sgi < nseg; ++sgi) {
         int c0 = sgi * seg_chunks;
@@ -1191,15 +1233,15 @@ hipError_t launch_prefill_ws(const StepArgs& a, void* ws, size_t ws_bytes, int n
         void* sout = last ? a.state : static_cast<void*>(stage);
         hipError_t e;
         if (!bf16)
-            e = launch_scan<float, float>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+            e = launch_scan<float, float>(tpw, ks, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
         else if (first && last)
-            e = launch_scan<uint16_t, uint16_t>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+            e = launch_scan<uint16_t, uint16_t>(tpw, ks, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
         else if (first)
-            e = launch_scan<uint16_t, float>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+            e = launch_scan<uint16_t, float>(tpw, ks, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
         else if (last)
-            e = launch_scan<float, uint16_t>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+            e = launch_scan<float, uint16_t>(tpw, ks, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
         else
-            e = launch_scan<float, float>(tpw, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
+            e = launch_scan<float, float>(tpw, ks, p, L, M, c0, nch, rec, sin, sout, last, units, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
