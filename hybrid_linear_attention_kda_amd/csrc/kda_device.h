@@ -71,17 +71,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
 
-// f32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two f32 -> packed bf16, lo in the low half: gfx950's v_cvt_pk_bf16_f32,
+// round to nearest even (the default rounding mode), subnormals kept, a NaN
+// stays a NaN of the same sign.  One VALU instruction per pair; a software
+// rounding of the bit pattern costs about six per value, and its NaN test
+// compiles to a branch per value.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-}
+// f32 -> bf16 (low 16 bits), as above.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 // Workgroup barrier that orders LDS only: global loads issued before it stay
 // in flight across it.

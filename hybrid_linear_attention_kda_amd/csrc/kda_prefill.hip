@@ -125,12 +125,8 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                    c, 0, 0, 0);
 }
 
-// two f32 -> packed bf16 (v_cvt_pk_bf16_f32, round to nearest even), a in the low half
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
-}
+// two f32 -> packed bf16, a in the low half
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) { return pack_bf16x2(a, b); }
 
 // the three bf16 pieces of (a, b), one packed dword each
 __device__ __forceinline__ void split2(float a, float b, uint32_t& p0, uint32_t& p1, uint32_t& p2) {

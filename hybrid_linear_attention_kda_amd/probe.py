@@ -125,10 +125,18 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser(description="HBM streaming probe sweep (one GPU)")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--chunk-mib", type=int, default=128,
+                    help="bytes per launch of the per-layer form (34 launches), MiB")
+    ap.add_argument("--kinds", default="0,1,2,3", help="comma-separated kinds: 0 in place, 1 read, 2 write, 3 copy")
+    ap.add_argument("--threads", default="256,512,1024")
+    ap.add_argument("--chunks", default="1,2,4")
+    ap.add_argument("--launches", default="per layer,one")
     ap.add_argument("--json", default=None, help="also write the rows to this file")
     a = ap.parse_args()
     if a.sweep:
-        out = sweep(reps=a.reps)
+        ints = lambda v: tuple(int(x) for x in v.split(","))  # noqa: E731
+        out = sweep(chunk_bytes=a.chunk_mib << 20, reps=a.reps, kinds=ints(a.kinds), threads=ints(a.threads),
+                    chunks=ints(a.chunks), launches=tuple(a.launches.split(",")))
         if a.json:
             with open(a.json, "w") as f:
                 json.dump(out, f, indent=1)
