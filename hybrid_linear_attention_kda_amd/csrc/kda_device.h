@@ -124,10 +124,27 @@ __device__ __forceinline__ float xor_reduce_from(float x) {
     }
 }
 
+// A DPP lane move within rows of 16 lanes (gfx9 control codes).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]: lane l reads l ^ 1
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]: lane l reads l ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane l reads 7 - l within its 8
+constexpr int kDppMirror = 0x140;      // lane l reads 15 - l within its 16
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the wave, the same in every lane, on the VALU: steps 1 and 2 swap
+// within quads; once the quads hold their sums, mirroring within 8 and then
+// within 16 lanes pairs each lane with the other quad (half) of its group,
+// exactly the partner that l ^ 4 (l ^ 8) names, so every step adds the same
+// two operands, in the same order, as the butterfly over l ^ 1 .. l ^ 32.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    x += dpp_mov<kDppQuadXor1>(x);
+    x += dpp_mov<kDppQuadXor2>(x);
+    x += dpp_mov<kDppHalfMirror>(x);
+    x += dpp_mov<kDppMirror>(x);
+    return xor_add<32>(xor_add<16>(x));
 }
 
 // Stores with agent scope (sc1) as well as the non-temporal hint.  On MI355X

@@ -312,13 +312,21 @@ __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&r
             wq[e] = fmaf(sv, qq, wq[e]);
         }
     }
-    // lanes that share columns differ in the bits above log2(CG)
+    // lanes that share columns differ in the bits above log2(CG).  Column
+    // splits (small grids, latency-bound) take the row and half-wave swaps
+    // on the VALU; whole heads keep the LDS permutes, which measured faster
+    // on the bandwidth-bound grids (M = 32 f32 48.2 against 48.3-48.4 us).
 #pragma unroll
-    for (int off = CG; off < 64; off <<= 1) {
+    for (int e = 0; e < VEC; ++e) {
+        if constexpr (G::NSPLIT_ > 1) {
+            u[e] = xor_reduce_from<CG>(u[e]);
+            wq[e] = xor_reduce_from<CG>(wq[e]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            u[e] += __shfl_xor(u[e], off, 64);
-            wq[e] += __shfl_xor(wq[e], off, 64);
+            for (int off = CG; off < 64; off <<= 1) {
+                u[e] += __shfl_xor(u[e], off, 64);
+                wq[e] += __shfl_xor(wq[e], off, 64);
+            }
         }
     }
 
@@ -558,9 +566,9 @@ __device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, 
             skk = fmaf(kv, kv, skk);
             sqk = fmaf(qv, kv, sqk);
         }
-        sqq = xor_reduce_from<1>(sqq);
-        skk = xor_reduce_from<1>(skk);
-        sqk = xor_reduce_from<1>(sqk);
+        sqq = wave_sum(sqq);
+        skk = wave_sum(skk);
+        sqk = wave_sum(sqk);
         if (lane == 0) {
             const float rq = p.scale * rsqrtf(sqq + 1e-6f), rk = rsqrtf(skk + 1e-6f);
             sm.rq[t] = rq;

@@ -210,6 +210,31 @@ def test_zero_input_is_pure_decay(state_dtype):
     assert torch.count_nonzero(lay.o.float()) == 0
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_bf16_state_rounding_ties(pow2):
+    """A pure decay by 1 + 2^-8 and 1 - 2^-8 leaves 8 bits below a bf16
+    state's last place: round to nearest even decides every element, and a
+    power-of-two state makes every one of the first kind an exact tie.  The
+    expected state is rounded on the CPU."""
+    wl = kda_synth.custom("ties", 2, 64, 128)
+    lay = Layer(wl, 0, DEV, "bf16")
+    if pow2:
+        e = torch.randint(-20, 4, lay.state.shape, generator=torch.Generator().manual_seed(5))
+        sign = torch.where(torch.rand(lay.state.shape, generator=torch.Generator().manual_seed(6)) < 0.5, -1.0, 1.0)
+        lay.state.copy_((sign * torch.pow(2.0, e.double())).to(torch.bfloat16))
+    lay.conv.zero_()
+    S0 = lay.state.cpu()
+    inp = kda_synth.step_inputs(wl, 0, 0, DEV)
+    inp["x"].zero_()
+    alpha = torch.full_like(inp["alpha"], 1.0 + 2.0 ** -8)
+    alpha[..., 1::2] = 1.0 - 2.0 ** -8
+    inp["alpha"].copy_(alpha)
+    lay.step(inp)
+    torch.cuda.synchronize()
+    expect = (S0.float() * alpha.cpu()[..., None]).to(torch.bfloat16)
+    assert torch.equal(lay.state.cpu(), expect)
+
+
 def test_exact_recall_beta1(orc):
     """beta = 1 and q = k (same channels, same conv taps, scale 1): the read
     returns v up to the L2 norm's epsilon ("GLM-5.3 deep dive" 8.2.3)."""
