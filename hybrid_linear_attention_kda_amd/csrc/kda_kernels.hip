@@ -492,9 +492,8 @@ __device__ __forceinline__ u32x2 seq_input(const Ptrs& p, int T, int m, size_t C
 }
 
 // Conv, alpha, beta and norms of tokens [c0, c0 + n) into LDS.
-template <class MG, int D, bool ALL = true>
-__device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, int c0, int n,
-                                            MultiSmem<MG, D>& sm) {
+template <class MG, int D, bool ALL = true, class SM = MultiSmem<MG, D>>
+__device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, int c0, int n, SM& sm) {
     typedef typename MG::G G;
     constexpr int IT = MG::ITEMS;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -722,6 +721,355 @@ void decode_multi_kernel(const Ptrs p, const int units, const int T)
     }
 }
 
+// -------------------------------------- T tokens per launch, chunk form --
+//
+// D = 128: the tokens of a (stream, head) pass through the state in chunks of
+// up to 8, each in the chunkwise form of the recurrence ("GLM-5.3 deep dive"
+// 8.2.5, Eq. 3-9, the WY representation; here without the division by the
+// cumulative decay, since a caller's alpha may be 0).  With S the state
+// before the chunk (rows i = key channels, columns j = value channels), token
+// t's decay g_t = a_t, the decay from token s to token t
+// g(t,s) = prod_{s<r<=t} a_r (per channel; g(t,t) = 1), and P_t = g(t,-1) the
+// decay of S itself up to token t:
+//   delta_t = beta_t (v_t - S^T (P_t k^_t) - sum_{s<t} (k^_s . g(t,s) k^_t) delta_s)
+//   o_t     = S^T (P_t q^_t) + sum_{s<=t} (k^_s . g(t,s) q^_t) delta_s
+//   S'      = Diag(P_{n-1}) S + sum_s (g(n-1,s) k^_s) delta_s^T
+// which is the token-by-token step (fade, predict, correct, write, read)
+// unrolled over the chunk.  The two state products, X = C^T S for the 16
+// vectors C = (P_t z_k,t | P_t z_q,t) and the rank-8 write, run on the f32
+// matrix cores (v_mfma_f32_16x16x4f32) straight from the state registers;
+// the 8 x 8 pair sums are sums over the channels, and the triangular solve
+// runs per value column.  z_k, z_q are the conv outputs before the L2 norms
+// (k^ = rk z_k, q^ = rq z_q), so the norms scale the small sums instead of
+// every row.
+//
+// State layout in registers (4 waves): wave w owns value columns
+// [32 w, 32 w + 32) for all 128 rows; lane (g = lane / 16, n = lane % 16)
+// holds rows 16 mb + 4 g + r (mb < 8, r < 4) and columns 32 w + 2 n + c
+// (c < 2), which is at once the B operand of X = C^T S (k index g at step
+// 4 mb + r) and the C / D operand of the write (row 4 g + r of tile mb).
+
+namespace wy {
+constexpr int D = 128, NT = 256, TC = 8;
+constexpr int CS = 20;                 // row stride of C (16 vectors + pad)
+constexpr int KS = 144;                // row stride of the write's A operand
+}
+
+struct WySmem {
+    // inputs of the chunk, as the serial kernel's chunk step writes them
+    __attribute__((aligned(16))) float z[wy::TC][3 * wy::D];   // q | k | v; each wave's X / Y tile later
+    __attribute__((aligned(16))) float a[wy::TC][wy::D];       // alpha; each wave's delta rows later
+    float b[wy::TC], rq[wy::TC], rk[wy::TC], kq[wy::TC];
+    __attribute__((aligned(16))) float C[wy::D][wy::CS];       // A operand of X: P_t z_k,t | P_t z_q,t
+    __attribute__((aligned(16))) float K[wy::TC][wy::KS];      // A operand of the write: g(n-1,s) z_k,s
+    __attribute__((aligned(16))) float G[wy::D];               // P_{n-1}
+    float red[4][2][16];                                       // pair sums per wave (64 channels each)
+};
+
+// The partner lane's value across lane bit B (B = 0, 1: quad swaps; 3: the
+// rotation by 8 within a row, which is l ^ 8).
+template <int B>
+__device__ __forceinline__ float xlane(float x) {
+    if constexpr (B == 0) return dpp_mov<kDppQuadXor1>(x);
+    else if constexpr (B == 1) return dpp_mov<kDppQuadXor2>(x);
+    else return dpp_mov<0x128>(x);
+}
+
+// One step of a transposed sum: the lane keeps half of its N values (the
+// low half if lane bit B is 0) and adds its partner's values of that half.
+template <int N, int B>
+__device__ __forceinline__ void tsum_step(float (&v)[16], int lane) {
+    constexpr int H = N / 2;
+    if constexpr (B == 4 || B == 5) {
+        // row / half-wave swap of (low, high): even rows (halves) end with
+        // both lows, odd ones with both highs
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const unsigned lo = __float_as_uint(v[k]), hi = __float_as_uint(v[k + H]);
+            const auto r = B == 4 ? __builtin_amdgcn_permlane16_swap(lo, hi, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+            v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    } else {
+        const bool up = (lane >> B) & 1;
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const float keep = up ? v[k + H] : v[k], send = up ? v[k] : v[k + H];
+            v[k] = keep + xlane<B>(send);
+        }
+    }
+}
+
+// Sums 16 values over the 64 lanes of a wave: lane l ends with the sum of
+// entry e(l) = 8 b4 + 4 b0 + 2 b1 + b3 (b_k = bit k of l).
+__device__ __forceinline__ float tsum16(float (&v)[16], int lane) {
+    tsum_step<16, 4>(v, lane);
+    tsum_step<8, 0>(v, lane);
+    tsum_step<4, 1>(v, lane);
+    tsum_step<2, 3>(v, lane);
+    float x = xor_add<32>(v[0]);
+    return x + __shfl_xor(x, 4, 64);
+}
+
+__device__ __forceinline__ int tsum16_entry(int lane) {
+    return ((lane >> 4) & 1) * 8 + (lane & 1) * 4 + ((lane >> 1) & 1) * 2 + ((lane >> 3) & 1);
+}
+
+template <typename TS> struct WyIO;
+template <> struct WyIO<float> {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef f2 raw_t;
+    static __device__ __forceinline__ raw_t load(const float* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const f2*>(p));
+    }
+    static __device__ __forceinline__ void unpack(raw_t r, float& x, float& y) { x = r.x; y = r.y; }
+    static __device__ __forceinline__ void store(float* p, float x, float y) {
+        __builtin_nontemporal_store(f2{x, y}, reinterpret_cast<f2*>(p));
+    }
+};
+template <> struct WyIO<uint16_t> {
+    typedef uint32_t raw_t;
+    static __device__ __forceinline__ raw_t load(const uint16_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    }
+    static __device__ __forceinline__ void unpack(raw_t r, float& x, float& y) { x = bf16_lo(r); y = bf16_hi(r); }
+    static __device__ __forceinline__ void store(uint16_t* p, float x, float y) {
+        __builtin_nontemporal_store(pack_bf16x2(x, y), reinterpret_cast<uint32_t*>(p));
+    }
+};
+
+// Pair index of (t, s), s < t < 8: t (t - 1) / 2 + s; pairs with t <= 5 form
+// batch 0 (indices 0..14), t = 6, 7 batch 1 (15..27).
+__device__ __forceinline__ constexpr int wy_pair(int t, int s) { return t * (t - 1) / 2 + s; }
+
+// Per-channel coefficients of one chunk of n tokens: thread (part, c), c the
+// channel.  Part 0 writes C and the k.k pair sums, part 1 K, G and the k.q
+// pair sums (both over the 64 channels of the wave, into red).
+__device__ __forceinline__ void wy_coeffs(int n, WySmem& sm) {
+    using namespace wy;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int c = tid & (D - 1), part = tid >> 7;
+    float av[TC], zk[TC], zq[TC];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+        const bool in = t < n;
+        av[t] = in ? sm.a[t][c] : 1.0f;
+        zk[t] = in ? sm.z[t][D + c] : 0.0f;
+        zq[t] = in ? sm.z[t][c] : 0.0f;
+    }
+    // pair sums: (t, s) -> g(t,s) z_k,s w_t, w = z_k (part 0) or z_q (part 1)
+    float pv[16];
+#pragma unroll
+    for (int bt = 0; bt < 2; ++bt) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) pv[k] = 0.0f;
+#pragma unroll
+        for (int t = 1; t < TC; ++t) {
+            if ((t <= 5) != (bt == 0)) continue;
+            const float w = part ? zq[t] : zk[t];
+            float g = 1.0f;
+#pragma unroll
+            for (int s = t - 1; s >= 0; --s) {
+                g *= av[s + 1];
+                pv[wy_pair(t, s) - 15 * bt] = g * zk[s] * w;
+            }
+        }
+        const float x = tsum16(pv, lane);
+        if ((lane & 0x24) == 0) sm.red[wv][bt][tsum16_entry(lane)] = x;
+    }
+    // prefix decays P_t: C (part 0); G and the write's coefficients (part 1)
+    if (part == 0) {
+        float P = 1.0f, ck[TC], cq[TC];
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+            P *= av[t];
+            ck[t] = P * zk[t];
+            cq[t] = P * zq[t];
+        }
+        f32x4* row = reinterpret_cast<f32x4*>(sm.C[c]);
+        row[0] = f32x4{ck[0], ck[1], ck[2], ck[3]};
+        row[1] = f32x4{ck[4], ck[5], ck[6], ck[7]};
+        row[2] = f32x4{cq[0], cq[1], cq[2], cq[3]};
+        row[3] = f32x4{cq[4], cq[5], cq[6], cq[7]};
+    } else {
+        float suf = 1.0f;
+#pragma unroll
+        for (int s = TC - 1; s >= 0; --s) {
+            sm.K[s][c] = suf * zk[s];              // 0 past the chunk's last token
+            if (s < n) suf *= av[s];
+        }
+        sm.G[c] = suf;                             // prod of a_0 .. a_{n-1}
+    }
+}
+
+// The state-dependent part of one chunk of n tokens (tokens c0 .. c0 + n - 1),
+// after wy_coeffs and a barrier: X = C^T S, the solve and the outputs, the
+// write.
+__device__ __forceinline__ void wy_chunk(float (&S)[8][4][2], const Ptrs& p, int T, int m, int h, int c0, int n,
+                                         WySmem& sm) {
+    using namespace wy;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, nn = lane & 15;
+    const size_t HD = (size_t)p.H * D;
+
+    // ---- X = C^T S: vectors 0..7 from z_k, 8..15 from z_q ----
+    f32x4 acc[2][2] = {};
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float a = sm.C[16 * mb + 4 * g + r][nn];
+            acc[0][mb & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, S[mb][r][0], acc[0][mb & 1], 0, 0, 0);
+            acc[1][mb & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, S[mb][r][1], acc[1][mb & 1], 0, 0, 0);
+        }
+    // the wave's X tile [16][32] goes to the q | k rows of z (dead now), its
+    // delta rows [8][32] to alpha's (dead too)
+    auto xy = [&](int v, int j) -> float& { return sm.z[2 * wv + (v >> 3)][(v & 7) * 32 + j]; };
+    auto drow = [&](int s, int j) -> float& { return sm.a[2 * wv + (s >> 2)][(s & 3) * 32 + j]; };
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const f32x4 x = acc[c][0] + acc[c][1];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xy(4 * g + r, 2 * nn + c) = x[r];
+    }
+
+    // the solve's coefficients, one per lane, read back by v_readlane:
+    // lane l < 8: token l's scalars; lane li = pair (< 15) or pair + 1 of the
+    // k.k sums times -rk_s rk_t, lane 32 + li of the k.q sums times rk_s rq_t
+    float cpair, ck_rk, ck_rq, ck_b, ck_diag;
+    {
+        const int pt = lane >> 5, bt = (lane >> 4) & 1, e = lane & 15;
+        const int pi = 15 * bt + e;                  // pair index (e == 15: padding)
+        int t = 1;
+        while (t < 7 && (t + 1) * t / 2 <= pi) ++t;
+        const int sidx = min(max(pi - t * (t - 1) / 2, 0), TC - 1);
+        const float sum = sm.red[2 * pt][bt][e] + sm.red[2 * pt + 1][bt][e];
+        cpair = pt == 0 ? -(sm.rk[sidx] * sm.rk[t]) * sum : (sm.rk[sidx] * sm.rq[t]) * sum;
+        const int tt = lane & 7;
+        ck_rk = sm.rk[tt];
+        ck_rq = sm.rq[tt];
+        ck_b = sm.b[tt];
+        ck_diag = sm.rk[tt] * sm.kq[tt];             // rk_t rq_t (z_k,t . z_q,t)
+    }
+    auto rl = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- the triangular solve and the outputs: lane j (and j + 32) takes column 32 wv + j ----
+    {
+        const int j = lane & 31;
+        float dl[TC];
+        uint16_t* const ou = p.o + ((size_t)m * T + c0) * HD + (size_t)h * D + 32 * wv + j;
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+            if (t < n) {
+                const float rk_t = rl(ck_rk, t);
+                float acc_d = fmaf(-rk_t, xy(t, j), sm.z[t][2 * D + 32 * wv + j]);
+                float acc_o = rl(ck_rq, t) * xy(8 + t, j);
+#pragma unroll
+                for (int s2 = 0; s2 < t; ++s2) {
+                    const int pi = t * (t - 1) / 2 + s2, li = pi < 15 ? pi : pi + 1;
+                    acc_d = fmaf(rl(cpair, li), dl[s2], acc_d);
+                    acc_o = fmaf(rl(cpair, 32 + li), dl[s2], acc_o);
+                }
+                dl[t] = rl(ck_b, t) * acc_d;
+                acc_o = fmaf(rl(ck_diag, t), dl[t], acc_o);
+                if (lane < 32) {
+                    ou[(size_t)t * HD] = (uint16_t)f32_to_bf16_rne(acc_o);
+                    drow(t, j) = rk_t * dl[t];
+                }
+            } else if (lane < 32) {
+                drow(t, j) = 0.0f;
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- S <- Diag(G) S + K^T E on the matrix cores ----
+    float e[2][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) e[st][c] = drow(4 * st + g, 2 * nn + c);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const f32x4 gd = *reinterpret_cast<const f32x4*>(&sm.G[16 * mb + 4 * g]);
+        const float k0 = sm.K[g][16 * mb + nn], k1 = sm.K[4 + g][16 * mb + nn];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            f32x4 cv = {S[mb][0][c] * gd[0], S[mb][1][c] * gd[1], S[mb][2][c] * gd[2], S[mb][3][c] * gd[3]};
+            cv = __builtin_amdgcn_mfma_f32_16x16x4f32(k0, e[0][c], cv, 0, 0, 0);
+            cv = __builtin_amdgcn_mfma_f32_16x16x4f32(k1, e[1][c], cv, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[mb][r][c] = cv[r];
+        }
+    }
+    // the next chunk overwrites the inputs, X, delta, C, K and G
+    lds_barrier();
+}
+
+template <typename TS>
+__global__ __launch_bounds__(wy::NT, 4)
+void decode_wy_kernel(const Ptrs p, const int units, const int T)
+{
+    using namespace wy;
+    typedef MultiGeo<TS, D, 4, 4, 1, TC> MG;
+    typedef WyIO<TS> IO;
+    __shared__ WySmem sm;
+    const int unit = (int)blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, nn = lane & 15;
+    const int m = unit / p.H, h = unit - m * p.H;
+    const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
+
+    float S[8][4][2];                                     // [mb][r][c]
+    {
+        // the first chunk's inputs and coefficients before the state is
+        // requested: a wave's loads complete in order
+        const int n = min(TC, T);
+        multi_chunk<MG, D, true, WySmem>(p, T, m, h, 0, n, sm);
+        wy_coeffs(n, sm);
+        const TS* st = static_cast<const TS*>(p.state) + (size_t)unit * D * D + 32 * wv + 2 * nn;
+        typename IO::raw_t raw[8][4];
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) raw[mb][r] = IO::load(st + (size_t)(16 * mb + 4 * g + r) * D);
+        lds_barrier();
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S[mb][r][0], S[mb][r][1]);
+        wy_chunk(S, p, T, m, h, 0, n, sm);
+    }
+    for (int c0 = TC; c0 < T; c0 += TC) {
+        const int n = min(TC, T - c0);
+        multi_chunk<MG, D, false, WySmem>(p, T, m, h, c0, n, sm);   // item by item beside the state
+        wy_coeffs(n, sm);
+        lds_barrier();
+        wy_chunk(S, p, T, m, h, c0, n, sm);
+    }
+
+    // the lane's state addresses, formed again here from a value the
+    // compiler cannot see into, so they are not kept live across the chunks
+    int lo = 32 * wv + 2 * nn + 4 * g * D;
+    asm volatile("" : "+v"(lo));
+    TS* const so = static_cast<TS*>(p.state) + (size_t)unit * D * D + lo;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) IO::store(so + (size_t)(16 * mb + r) * D, S[mb][r][0], S[mb][r][1]);
+    if (tid < MG::NGT) {
+        const size_t ch = group_channel<typename MG::G, D>(tid, h, 0, HD);
+        const u32x2 n0 = seq_input(p, T, m, C3, ch, T - 3);
+        const u32x2 n1 = seq_input(p, T, m, C3, ch, T - 2);
+        const u32x2 n2 = seq_input(p, T, m, C3, ch, T - 1);
+        uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + ch;
+        st8(co, n0);
+        st8(co + C3, n1);
+        st8(co + 2 * C3, n2);
+    }
+}
+
 // -------------------------------------------------------------- conv step --
 // One thread per 8 consecutive channels of one stream.
 __global__ __launch_bounds__(256)
@@ -857,6 +1205,16 @@ static hipError_t launch_multi(const StepArgs& a) {
                            dim3((unsigned)units), dim3(NWAVES * 64), args, 0, (hipStream_t)a.stream);
 }
 
+template <typename TS>
+static hipError_t launch_wy(const StepArgs& a) {
+    Ptrs p = make_ptrs(a);
+    int units = a.M * a.H;
+    int T = a.T;
+    void* args[] = {(void*)&p, (void*)&units, (void*)&T};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_wy_kernel<TS>), dim3((unsigned)units),
+                           dim3(wy::NT), args, 0, (hipStream_t)a.stream);
+}
+
 // T tokens per launch, one workgroup per head.
 hipError_t launch_decode_multi(const StepArgs& a) {
     const bool f32 = a.state_dtype == 0;
@@ -865,13 +1223,8 @@ hipError_t launch_decode_multi(const StepArgs& a) {
     case 32: return f32 ? launch_multi<float, 32, 1, 4, 0, 2>(a) : launch_multi<uint16_t, 32, 1, 8, 0, 2>(a);
     case 64: return f32 ? launch_multi<float, 64, 2, 4, 0, 2>(a) : launch_multi<uint16_t, 64, 2, 8, 0, 2>(a);
     case 128:
-        // 4 waves per head, each wave a band of rows, 16 rows x 4 columns per
-        // lane for either state type (8-byte accesses for bf16: with 8
-        // columns per lane a row spans 16 lanes and every column sum takes
-        // two cross-lane steps instead of one); the token loop is
-        // latency-bound, so more heads per CU beat more waves per head
-        // (measured)
-        return f32 ? launch_multi<float, 128, 4, 4, 1, 8>(a) : launch_multi<uint16_t, 128, 4, 4, 1, 8>(a);
+        // the chunk form: 4 waves per head, 8-token chunks
+        return f32 ? launch_wy<float>(a) : launch_wy<uint16_t>(a);
     default: return hipErrorInvalidValue;
     }
 }
