@@ -492,8 +492,13 @@ __device__ __forceinline__ u32x2 seq_input(const Ptrs& p, int T, int m, size_t C
 }
 
 // Conv, alpha, beta and norms of tokens [c0, c0 + n) into LDS.
-template <class MG, int D, bool ALL = true, class SM = MultiSmem<MG, D>>
-__device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, int c0, int n, SM& sm) {
+struct NoLoads {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+template <class MG, int D, bool ALL = true, class SM = MultiSmem<MG, D>, class After = NoLoads>
+__device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, int c0, int n, SM& sm,
+                                            After after = After()) {
     typedef typename MG::G G;
     constexpr int IT = MG::ITEMS;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -544,6 +549,7 @@ __device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, 
         Item its[IT];
 #pragma unroll
         for (int k = 0; k < IT; ++k) load_item(k, its[k]);
+        after();                         // loads the caller issues behind the items'
 #pragma unroll
         for (int k = 0; k < IT; ++k) conv_item(k, its[k]);
     } else {
@@ -1007,7 +1013,12 @@ __device__ __forceinline__ void wy_chunk(float (&S)[8][4][2], const Ptrs& p, int
     lds_barrier();
 }
 
-template <typename TS>
+// ONE: T <= 8, a single chunk, its state requested in two halves, the first
+// right behind the chunk's input loads and the second once their registers
+// are free, so the state streams in while the inputs wait and the
+// coefficients are formed.  Otherwise chunk after chunk, the state requested
+// once the first chunk's coefficients are formed.
+template <typename TS, bool ONE>
 __global__ __launch_bounds__(wy::NT, 4)
 void decode_wy_kernel(const Ptrs p, const int units, const int T)
 {
@@ -1022,7 +1033,29 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
     const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
 
     float S[8][4][2];                                     // [mb][r][c]
-    {
+    if constexpr (ONE) {
+        const TS* st = static_cast<const TS*>(p.state) + (size_t)unit * D * D + 32 * wv + 2 * nn;
+        typename IO::raw_t raw[8][4];
+        auto half = [&](int h2) {
+#pragma unroll
+            for (int mb = 4 * h2; mb < 4 * h2 + 4; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) raw[mb][r] = IO::load(st + (size_t)(16 * mb + 4 * g + r) * D);
+        };
+        // (bf16: the whole state fits beside the chunk's input registers)
+        multi_chunk<MG, D, true, WySmem>(p, T, m, h, 0, T, sm, [&]() {
+            half(0);
+            if constexpr (sizeof(TS) == 2) half(1);
+        });
+        if constexpr (sizeof(TS) == 4) half(1);
+        wy_coeffs(T, sm);
+        lds_barrier();
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S[mb][r][0], S[mb][r][1]);
+        wy_chunk(S, p, T, m, h, 0, T, sm);
+    } else {
         // the first chunk's inputs and coefficients before the state is
         // requested: a wave's loads complete in order
         const int n = min(TC, T);
@@ -1040,13 +1073,13 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
 #pragma unroll
             for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S[mb][r][0], S[mb][r][1]);
         wy_chunk(S, p, T, m, h, 0, n, sm);
-    }
-    for (int c0 = TC; c0 < T; c0 += TC) {
-        const int n = min(TC, T - c0);
-        multi_chunk<MG, D, false, WySmem>(p, T, m, h, c0, n, sm);   // item by item beside the state
-        wy_coeffs(n, sm);
-        lds_barrier();
-        wy_chunk(S, p, T, m, h, c0, n, sm);
+        for (int c0 = TC; c0 < T; c0 += TC) {
+            const int n2 = min(TC, T - c0);
+            multi_chunk<MG, D, false, WySmem>(p, T, m, h, c0, n2, sm);   // item by item beside the state
+            wy_coeffs(n2, sm);
+            lds_barrier();
+            wy_chunk(S, p, T, m, h, c0, n2, sm);
+        }
     }
 
     // the lane's state addresses, formed again here from a value the
@@ -1211,8 +1244,9 @@ static hipError_t launch_wy(const StepArgs& a) {
     int units = a.M * a.H;
     int T = a.T;
     void* args[] = {(void*)&p, (void*)&units, (void*)&T};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_wy_kernel<TS>), dim3((unsigned)units),
-                           dim3(wy::NT), args, 0, (hipStream_t)a.stream);
+    const void* fn = T <= wy::TC ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, true>)
+                                 : reinterpret_cast<const void*>(&decode_wy_kernel<TS, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)units), dim3(wy::NT), args, 0, (hipStream_t)a.stream);
 }
 
 // T tokens per launch, one workgroup per head.
