@@ -131,12 +131,13 @@ if __name__ == "__main__":
     ap.add_argument("--threads", default="256,512,1024")
     ap.add_argument("--chunks", default="1,2,4")
     ap.add_argument("--launches", default="per layer,one")
+    ap.add_argument("--persistent", default="0,1", help="comma-separated: 0 one workgroup per tile, 1 grid-stride")
     ap.add_argument("--json", default=None, help="also write the rows to this file")
     a = ap.parse_args()
     if a.sweep:
         ints = lambda v: tuple(int(x) for x in v.split(","))  # noqa: E731
         out = sweep(chunk_bytes=a.chunk_mib << 20, reps=a.reps, kinds=ints(a.kinds), threads=ints(a.threads),
-                    chunks=ints(a.chunks), launches=tuple(a.launches.split(",")))
+                    chunks=ints(a.chunks), persistent=ints(a.persistent), launches=tuple(a.launches.split(",")))
         if a.json:
             with open(a.json, "w") as f:
                 json.dump(out, f, indent=1)
