@@ -5,8 +5,9 @@ One "step" is one token through all 34 KDA layers of GLM-5.3-Flash: 34
 launches of the fused decode kernel, each over M streams x 64 heads x
 128 x 128 state, every layer with its own state (so the state is read from
 HBM, not from the 256 MiB Infinity Cache).  Inputs are synthetic
-(``kda_synth``), resident in HBM before timing starts; 8 input sets (fresh
-q/k/v, alpha, beta per step) rotate across steps.
+(``kda_synth``), resident in HBM before timing starts: the headline draws a
+fresh input set (q/k/v, alpha, beta) for every timed step; the secondary
+lines rotate up to 8 sets.
 
 Headline: M = 32 streams, FP32 state.  Also measured (``secondary``): M = 8
 with FP32 and BF16 state, M = 128 with BF16 state, M = 1, the gated and
@@ -637,7 +638,8 @@ def main():
         return
 
     wl = kda_synth.WORKLOADS["glm_m32"]
-    log(f"headline: {wl.description}")
+    log(f"headline: {wl.description}; timed: {args.steps} steps after {args.warmup} warm-up steps, "
+        f"a fresh input set for every timed step")
     # fresh q/k/v, alpha and beta for every timed step (input set k for timed step k)
     head = measure(wl, "f32", args.steps, args.warmup, n_inputs=args.steps, check=True)
     log(f"  {json.dumps({k: head[k] for k in ('launch', 'ms_per_step', 'ms_per_layer', 'state_GBps')})}")
