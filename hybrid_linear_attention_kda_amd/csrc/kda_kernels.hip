@@ -1190,10 +1190,13 @@ static hipError_t launch_decode(const StepArgs& a) {
 //    round of workgroups over every CU (256 to 768 heads at 3 per CU: 4%
 //    faster at 512), interleaved rows otherwise (fewer heads: idle CUs;
 //    more: several rounds; both slower with bands).
-//  bf16, whole head per workgroup: 8 waves, each owning a band of 16 rows,
-//    8 rows x 4 columns per lane (8-byte accesses; with 8 columns per lane
-//    and 16-byte accesses a row spans 16 lanes and the column sums take two
-//    cross-lane steps: slower at every M measured).
+//  bf16, whole head per workgroup: 4 waves, each owning a band of 32 rows,
+//    16 rows x 4 columns per lane (8-byte accesses), 4 workgroups per CU:
+//    against 8 waves of 8 rows, M = 8 7.70 / 7.81 us, M = 32 26.1 / 26.7,
+//    M = 128 97.4 / 98.0 (with the hardware bf16 rounding; before it the
+//    8-wave form was the faster one).  With 8 columns per lane and 16-byte
+//    accesses a row spans 16 lanes and the column sums take two cross-lane
+//    steps: slower at every M measured.
 //  column splits (small M*H only): 8 waves (f32, 2-way), else 4 waves.
 //  state stores with agent scope (WT) once there are >= 2048 heads, i.e.
 //    several rounds of workgroups per CU: 1.5% faster at 32 x 64 heads (f32)
@@ -1221,8 +1224,8 @@ static hipError_t dispatch_wide_f32(const StepArgs& a) {
 template <bool FUSED, int MODE>
 static hipError_t dispatch_wide_bf16(const StepArgs& a) {
     if (a.nsplit == 1)
-        return (long)a.M * a.H >= 2048 ? launch_decode<uint16_t, 128, 1, 8, 4, FUSED, false, 1, MODE, true>(a)
-                                       : launch_decode<uint16_t, 128, 1, 8, 4, FUSED, false, 1, MODE>(a);
+        return (long)a.M * a.H >= 2048 ? launch_decode<uint16_t, 128, 1, 4, 4, FUSED, false, 1, MODE, true>(a)
+                                       : launch_decode<uint16_t, 128, 1, 4, 4, FUSED, false, 1, MODE>(a);
     if constexpr (MODE != 2) {
         if (a.nsplit == 2) return launch_decode<uint16_t, 128, 2, 4, 8, FUSED, true, 0, MODE>(a);
         if (a.nsplit == 4) return launch_decode<uint16_t, 128, 4, 4, 8, FUSED, true, 0, MODE>(a);
