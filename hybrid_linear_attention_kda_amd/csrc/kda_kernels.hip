@@ -1184,12 +1184,13 @@ static hipError_t launch_decode(const StepArgs& a) {
 
 // D = 128 launch shapes, from measurement on MI355X (34 layers of distinct
 // state, DRAM-resident):
-//  f32, whole head per workgroup: 8 waves (8 rows x 4 columns per lane); 16
-//    waves (4 rows per lane) once there are >= 2048 heads to run.  With 8
-//    waves, each wave takes a band of rows (RMAP 1) when the grid is one
-//    round of workgroups over every CU (256 to 768 heads at 3 per CU: 4%
-//    faster at 512), interleaved rows otherwise (fewer heads: idle CUs;
-//    more: several rounds; both slower with bands).
+//  f32, whole head per workgroup: 16 waves (4 rows x 4 columns per lane)
+//    once there are >= 2048 heads to run; 4 waves, each a band of 32 rows
+//    (16 rows per lane, 4 workgroups per CU), for 256 to 768 heads, one
+//    round of workgroups (M = 8: 12.35 against 12.6 us with 8 waves of 8
+//    rows in bands, itself 4% faster than interleaved rows there); else 8
+//    waves with interleaved rows (fewer heads: idle CUs; more: several
+//    rounds; both slower with bands).
 //  bf16, whole head per workgroup: 4 waves, each owning a band of 32 rows,
 //    16 rows x 4 columns per lane (8-byte accesses), 4 workgroups per CU:
 //    against 8 waves of 8 rows, M = 8 7.70 / 7.81 us, M = 32 26.1 / 26.7,
@@ -1211,7 +1212,7 @@ static hipError_t dispatch_wide_f32(const StepArgs& a) {
     if (a.nsplit == 1) {
         const long heads = (long)a.M * a.H;
         if (heads >= 2048) return launch_decode<float, 128, 1, 16, 4, FUSED, false, 0, MODE, true>(a);
-        if (heads >= 256 && heads <= 768) return launch_decode<float, 128, 1, 8, 4, FUSED, false, 1, MODE>(a);
+        if (heads >= 256 && heads <= 768) return launch_decode<float, 128, 1, 4, 4, FUSED, false, 1, MODE>(a);
         return launch_decode<float, 128, 1, 8, 4, FUSED, false, 0, MODE>(a);
     }
     if constexpr (MODE != 2) {
