@@ -1284,8 +1284,24 @@ hipError_t launch_decode_multi(const StepArgs& a) {
     case 32: return f32 ? launch_multi<float, 32, 1, 4, 0, 2>(a) : launch_multi<uint16_t, 32, 1, 8, 0, 2>(a);
     case 64: return f32 ? launch_multi<float, 64, 2, 4, 0, 2>(a) : launch_multi<uint16_t, 64, 2, 8, 0, 2>(a);
     case 128:
-        // the chunk form: 4 waves per head, 8-token chunks
-        return f32 ? launch_wy<float>(a) : launch_wy<uint16_t>(a);
+        // 4 waves per head either way.  The chunk form pays its matrix
+        // products per chunk, the token loop its sweep per token; measured
+        // on MI355X (us per call, token loop / chunk form, 34 layers):
+        //   f32, M = 32:   T = 1 50.9 / 51.3, 2 53.8 / 53.2, 4 57.3 / 55.3,
+        //                  8 69.0 / 59.3, 9 76.3 / 77.3, 16 104.5 / 89.3,
+        //                  17 110.3 / 105.4, 32 176.8 / 151.6
+        //   bf16, M = 128: T = 1 98.5 / 126.4, 4 126.9 / 144.6, 6 159.0 / 154.5,
+        //                  8 190.5 / 166.3, 9 216.1 / 241.5, 12 263.5 / 261.1,
+        //                  16 329.4 / 286.1, 17 352.6 / 356.7, 20 407.0 / 376.0,
+        //                  32 611.7 / 513.1
+        // so f32 takes the chunk form from T = 2 on, and bf16 where
+        // 116 ceil(T / 8) < 17.5 T + 30 (the fitted per-chunk and per-token
+        // costs at M = 128): T = 5..8, 12..16 and every T >= 19.
+        if (f32) return a.T >= 2 ? launch_wy<float>(a) : launch_multi<float, 128, 4, 4, 1, 8>(a);
+        {
+            const long chunks = ((long)a.T + wy::TC - 1) / wy::TC;
+            return 232 * chunks < 35L * a.T + 60 ? launch_wy<uint16_t>(a) : launch_multi<uint16_t, 128, 4, 4, 1, 8>(a);
+        }
     default: return hipErrorInvalidValue;
     }
 }
