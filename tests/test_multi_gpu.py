@@ -162,9 +162,11 @@ def test_multi_fade_extremes(orc, M, H, D, T, state_dtype, case):
 
 
 # Token counts around the D = 128 kernel's 8-token chunks: one chunk plus one
-# token, two full chunks, two plus one, and a ragged third.
+# token, two full chunks, two plus one, and a ragged third; and on both sides
+# of the T at which the bf16 state switches between the token loop and the
+# chunk form (4 | 5, 11 | 12, 18 | 19).
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T", [9, 16, 17, 23])
+@pytest.mark.parametrize("T", [4, 5, 9, 11, 12, 16, 17, 18, 19, 23])
 def test_multi_chunk_boundaries(orc, T, state_dtype):
     M, H, D = 2, 3, 128
     wl = kda_synth.custom(f"multi_bound_{T}", M, H, D, steps=T)
