@@ -759,6 +759,13 @@ namespace wy {
 constexpr int D = 128, NT = 256, TC = 8;
 constexpr int CS = 20;                 // row stride of C (16 vectors + pad)
 constexpr int KS = 144;                // row stride of the write's A operand
+constexpr int CBS = 136;               // vector stride of the bf16 pieces of C (128 slots + pad)
+// Row slot of key row i in the bf16 pieces of C: lane group g of a 32-row
+// block j reads slots 32 j + 8 g .. + 7, which are the rows 32 j + 4 g + r
+// and 32 j + 16 + 4 g + r (r < 4) that its state registers hold.
+__device__ __forceinline__ int cb_slot(int i) {
+    return (i & ~31) | (((i >> 2) & 3) << 3) | (((i >> 4) & 1) << 2) | (i & 3);
+}
 }
 
 struct WySmem {
@@ -766,7 +773,11 @@ struct WySmem {
     __attribute__((aligned(16))) float z[wy::TC][3 * wy::D];   // q | k | v; each wave's X / Y tile later
     __attribute__((aligned(16))) float a[wy::TC][wy::D];       // alpha; each wave's delta rows later
     float b[wy::TC], rq[wy::TC], rk[wy::TC], kq[wy::TC];
-    __attribute__((aligned(16))) float C[wy::D][wy::CS];       // A operand of X: P_t z_k,t | P_t z_q,t
+    union {
+        __attribute__((aligned(16))) float C[wy::D][wy::CS];   // A operand of X: P_t z_k,t | P_t z_q,t
+        // the same as three bf16 pieces (bf16 state, one chunk), [piece][vector][row slot]
+        __attribute__((aligned(16))) uint16_t Cb[3][16][wy::CBS];
+    };
     __attribute__((aligned(16))) float K[wy::TC][wy::KS];      // A operand of the write: g(n-1,s) z_k,s
     __attribute__((aligned(16))) float G[wy::D];               // P_{n-1}
     float red[4][2][16];                                       // pair sums per wave (64 channels each)
@@ -851,6 +862,7 @@ __device__ __forceinline__ constexpr int wy_pair(int t, int s) { return t * (t -
 // Per-channel coefficients of one chunk of n tokens: thread (part, c), c the
 // channel.  Part 0 writes C and the k.k pair sums, part 1 K, G and the k.q
 // pair sums (both over the 64 channels of the wave, into red).
+template <bool XB = false>
 __device__ __forceinline__ void wy_coeffs(int n, WySmem& sm) {
     using namespace wy;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -892,11 +904,31 @@ __device__ __forceinline__ void wy_coeffs(int n, WySmem& sm) {
             ck[t] = P * zk[t];
             cq[t] = P * zq[t];
         }
-        f32x4* row = reinterpret_cast<f32x4*>(sm.C[c]);
-        row[0] = f32x4{ck[0], ck[1], ck[2], ck[3]};
-        row[1] = f32x4{ck[4], ck[5], ck[6], ck[7]};
-        row[2] = f32x4{cq[0], cq[1], cq[2], cq[3]};
-        row[3] = f32x4{cq[4], cq[5], cq[6], cq[7]};
+        if constexpr (XB) {
+            // three bf16 pieces per value (round to nearest even; each
+            // remainder is exact in f32), vector v at slot cb_slot(c)
+            const int sl = cb_slot(c);
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const float x0 = v < 8 ? ck[v] : cq[v - 8], x1 = v < 8 ? ck[v + 1] : cq[v - 7];
+                const uint32_t p0 = pack_bf16x2(x0, x1);
+                const float r0 = x0 - bf16_lo(p0), r1 = x1 - bf16_hi(p0);
+                const uint32_t p1 = pack_bf16x2(r0, r1);
+                const uint32_t p2 = pack_bf16x2(r0 - bf16_lo(p1), r1 - bf16_hi(p1));
+                sm.Cb[0][v][sl] = (uint16_t)p0;
+                sm.Cb[0][v + 1][sl] = (uint16_t)(p0 >> 16);
+                sm.Cb[1][v][sl] = (uint16_t)p1;
+                sm.Cb[1][v + 1][sl] = (uint16_t)(p1 >> 16);
+                sm.Cb[2][v][sl] = (uint16_t)p2;
+                sm.Cb[2][v + 1][sl] = (uint16_t)(p2 >> 16);
+            }
+        } else {
+            f32x4* row = reinterpret_cast<f32x4*>(sm.C[c]);
+            row[0] = f32x4{ck[0], ck[1], ck[2], ck[3]};
+            row[1] = f32x4{ck[4], ck[5], ck[6], ck[7]};
+            row[2] = f32x4{cq[0], cq[1], cq[2], cq[3]};
+            row[3] = f32x4{cq[4], cq[5], cq[6], cq[7]};
+        }
     } else {
         float suf = 1.0f;
 #pragma unroll
@@ -911,14 +943,50 @@ __device__ __forceinline__ void wy_coeffs(int n, WySmem& sm) {
 // The state-dependent part of one chunk of n tokens (tokens c0 .. c0 + n - 1),
 // after wy_coeffs and a barrier: X = C^T S, the solve and the outputs, the
 // write.
+// The state's registers in the chunk form: lane (g, n) holds rows
+// 16 mb + 4 g + r and columns 32 w + 2 n + c.  F32Regs keeps them as f32.
+// PackedRegs keeps each row's column pair as the two bf16 of a bf16 state's
+// single chunk: one VGPR instead of two; X = C^T S then runs on the bf16
+// matrix cores (the state is exact in bf16, C goes as three bf16 pieces:
+// 24 v_mfma_f32_16x16x32_bf16 per wave instead of 64 f32 MFMAs), and the
+// write widens each tile, updates it in f32 and rounds it once -- the same
+// single rounding the state gets on its way back to memory.
+struct F32Regs {
+    static constexpr bool XB = false;
+    float v[8][4][2];
+    __device__ __forceinline__ float get(int mb, int r, int c) const { return v[mb][r][c]; }
+    __device__ __forceinline__ void set(int mb, int r, float x0, float x1) { v[mb][r][0] = x0; v[mb][r][1] = x1; }
+    template <typename TS>
+    __device__ __forceinline__ void store(TS* p, int mb, int r) const { WyIO<TS>::store(p, v[mb][r][0], v[mb][r][1]); }
+};
+struct PackedRegs {
+    static constexpr bool XB = true;
+    uint32_t v[8][4];
+    __device__ __forceinline__ float get(int mb, int r, int c) const {
+        return c ? bf16_hi(v[mb][r]) : bf16_lo(v[mb][r]);
+    }
+    __device__ __forceinline__ void set(int mb, int r, float x0, float x1) { v[mb][r] = pack_bf16x2(x0, x1); }
+    __device__ __forceinline__ void store(uint16_t* p, int mb, int r) const {
+        __builtin_nontemporal_store(v[mb][r], reinterpret_cast<uint32_t*>(p));
+    }
+    // B fragment of 32-row block j, column c: k slot i of lane group g is row
+    // 32 j + 16 (i / 4) + 4 g + i % 4, two bf16 per dword
+    __device__ __forceinline__ u32x4 bfrag(int j, int c) const {
+        const uint32_t sel = c ? 0x07060302u : 0x05040100u;   // high or low halves of (x, y) -> y:x
+        return u32x4{__builtin_amdgcn_perm(v[2 * j][1], v[2 * j][0], sel),
+                     __builtin_amdgcn_perm(v[2 * j][3], v[2 * j][2], sel),
+                     __builtin_amdgcn_perm(v[2 * j + 1][1], v[2 * j + 1][0], sel),
+                     __builtin_amdgcn_perm(v[2 * j + 1][3], v[2 * j + 1][2], sel)};
+    }
+};
+
 // STORE: the last chunk, which stores the new state: f32 each row tile as
 // soon as its products are done, so the stores overlap the remaining ones
 // (M = 32, T = 8: 58.1 against 58.6 us); bf16 after the last tile and a
 // barrier, so that the two waves whose 64-byte pieces share each 128-byte
 // line store together (M = 128, T = 8: 164.2 against 166.6 us without).
-template <typename TS, bool STORE>
-__device__ __forceinline__ void wy_chunk(float (&S)[8][4][2], const Ptrs& p, int T, int m, int h, int c0, int n,
-                                         WySmem& sm) {
+template <typename TS, bool STORE, class SR>
+__device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int h, int c0, int n, WySmem& sm) {
     using namespace wy;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 4, nn = lane & 15;
@@ -926,14 +994,30 @@ __device__ __forceinline__ void wy_chunk(float (&S)[8][4][2], const Ptrs& p, int
 
     // ---- X = C^T S: vectors 0..7 from z_k, 8..15 from z_q ----
     f32x4 acc[2][2] = {};
+    if constexpr (SR::XB) {
+        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 b0 = S.bfrag(j, 0), b1 = S.bfrag(j, 1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float a = sm.C[16 * mb + 4 * g + r][nn];
-            acc[0][mb & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, S[mb][r][0], acc[0][mb & 1], 0, 0, 0);
-            acc[1][mb & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, S[mb][r][1], acc[1][mb & 1], 0, 0, 0);
+            for (int pc = 0; pc < 3; ++pc) {
+                const u32x4 af = *reinterpret_cast<const u32x4*>(&sm.Cb[pc][nn][32 * j + 8 * g]);
+                acc[0][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, b0), acc[0][j & 1], 0, 0, 0);
+                acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, b1), acc[1][j & 1], 0, 0, 0);
+            }
         }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a = sm.C[16 * mb + 4 * g + r][nn];
+                acc[0][mb & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, S.get(mb, r, 0), acc[0][mb & 1], 0, 0, 0);
+                acc[1][mb & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, S.get(mb, r, 1), acc[1][mb & 1], 0, 0, 0);
+            }
+    }
     // the wave's X tile [16][32] goes to the q | k rows of z (dead now), its
     // delta rows [8][32] to alpha's (dead too)
     auto xy = [&](int v, int j) -> float& { return sm.z[2 * wv + (v >> 3)][(v & 7) * 32 + j]; };
@@ -1014,17 +1098,19 @@ __device__ __forceinline__ void wy_chunk(float (&S)[8][4][2], const Ptrs& p, int
     for (int mb = 0; mb < 8; ++mb) {
         const f32x4 gd = *reinterpret_cast<const f32x4*>(&sm.G[16 * mb + 4 * g]);
         const float k0 = sm.K[g][16 * mb + nn], k1 = sm.K[4 + g][16 * mb + nn];
+        f32x4 cv[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            f32x4 cv = {S[mb][0][c] * gd[0], S[mb][1][c] * gd[1], S[mb][2][c] * gd[2], S[mb][3][c] * gd[3]};
-            cv = __builtin_amdgcn_mfma_f32_16x16x4f32(k0, e[0][c], cv, 0, 0, 0);
-            cv = __builtin_amdgcn_mfma_f32_16x16x4f32(k1, e[1][c], cv, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[mb][r][c] = cv[r];
+            cv[c] = f32x4{S.get(mb, 0, c) * gd[0], S.get(mb, 1, c) * gd[1], S.get(mb, 2, c) * gd[2],
+                          S.get(mb, 3, c) * gd[3]};
+            cv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(k0, e[0][c], cv[c], 0, 0, 0);
+            cv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(k1, e[1][c], cv[c], 0, 0, 0);
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.set(mb, r, cv[0][r], cv[1][r]);
         if constexpr (STORE && sizeof(TS) == 4) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) WyIO<TS>::store(so + (size_t)(16 * mb + r) * D, S[mb][r][0], S[mb][r][1]);
+            for (int r = 0; r < 4; ++r) S.store(so + (size_t)(16 * mb + r) * D, mb, r);
         }
     }
     if constexpr (STORE && sizeof(TS) == 2) {
@@ -1032,7 +1118,7 @@ __device__ __forceinline__ void wy_chunk(float (&S)[8][4][2], const Ptrs& p, int
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) WyIO<TS>::store(so + (size_t)(16 * mb + r) * D, S[mb][r][0], S[mb][r][1]);
+            for (int r = 0; r < 4; ++r) S.store(so + (size_t)(16 * mb + r) * D, mb, r);
     }
     // the next chunk overwrites the inputs, X, delta, C, K and G
     if constexpr (!STORE) lds_barrier();
@@ -1057,7 +1143,6 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
     const int m = unit / p.H, h = unit - m * p.H;
     const size_t HD = (size_t)p.H * D, C3 = 3 * HD;
 
-    float S[8][4][2];                                     // [mb][r][c]
     if constexpr (ONE) {
         const TS* st = static_cast<const TS*>(p.state) + (size_t)unit * D * D + 32 * wv + 2 * nn;
         typename IO::raw_t raw[8][4];
@@ -1072,15 +1157,28 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
             half(0);
             if constexpr (sizeof(TS) == 2) half(1);
         });
-        if constexpr (sizeof(TS) == 4) half(1);
-        wy_coeffs(T, sm);
-        lds_barrier();
+        if constexpr (sizeof(TS) == 4) {
+            half(1);
+            wy_coeffs(T, sm);
+            lds_barrier();
+            F32Regs S;
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+            for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S[mb][r][0], S[mb][r][1]);
-        wy_chunk<TS, true>(S, p, T, m, h, 0, T, sm);
+                for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S.v[mb][r][0], S.v[mb][r][1]);
+            wy_chunk<TS, true>(S, p, T, m, h, 0, T, sm);
+        } else {
+            wy_coeffs<true>(T, sm);
+            lds_barrier();
+            PackedRegs S;
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S.v[mb][r] = raw[mb][r];
+            wy_chunk<TS, true>(S, p, T, m, h, 0, T, sm);
+        }
     } else {
+        F32Regs S;
         // the first chunk's inputs and coefficients before the state is
         // requested: a wave's loads complete in order
         const int n = min(TC, T);
@@ -1096,7 +1194,7 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S[mb][r][0], S[mb][r][1]);
+            for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S.v[mb][r][0], S.v[mb][r][1]);
         wy_chunk<TS, false>(S, p, T, m, h, 0, n, sm);
         for (int c0 = TC; c0 < T; c0 += TC) {
             const int n2 = min(TC, T - c0);
@@ -1111,7 +1209,7 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) IO::store(so + (size_t)(16 * mb + r) * D, S[mb][r][0], S[mb][r][1]);
+            for (int r = 0; r < 4; ++r) IO::store(so + (size_t)(16 * mb + r) * D, S.v[mb][r][0], S.v[mb][r][1]);
     }
 
     if (tid < MG::NGT) {
