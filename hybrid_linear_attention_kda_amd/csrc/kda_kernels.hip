@@ -1388,10 +1388,11 @@ hipError_t launch_decode_multi(const StepArgs& a) {
         //   f32, M = 32:   T = 1 50.9 / 51.3, 2 53.8 / 53.2, 4 57.3 / 55.3,
         //                  8 69.0 / 59.3, 9 76.3 / 77.3, 16 104.5 / 89.3,
         //                  17 110.3 / 105.4, 32 176.8 / 151.6
-        //   bf16, M = 128: T = 1 98.5 / 126.4, 4 126.9 / 144.6, 6 159.0 / 154.5,
-        //                  8 190.5 / 166.3, 9 216.1 / 241.5, 12 263.5 / 261.1,
-        //                  16 329.4 / 286.1, 17 352.6 / 356.7, 20 407.0 / 376.0,
-        //                  32 611.7 / 513.1
+        //   bf16, M = 128: T = 1 97.8 / 125.0, 2 103.2 / 131.7, 4 128.6 / 136.1,
+        //                  5 138.2 / 138.1, 6 146.2 / 144.8, 8 190.5 / 154
+        //                  (one chunk: X on the bf16 matrix cores), 9 216.1 /
+        //                  241.5, 12 263.5 / 261.1, 16 329.4 / 286.1, 17 352.6 /
+        //                  356.7, 20 407.0 / 376.0, 32 611.7 / 513.1
         // so f32 takes the chunk form from T = 2 on, and bf16 where
         // 116 ceil(T / 8) < 17.5 T + 30 (the fitted per-chunk and per-token
         // costs at M = 128): T = 5..8, 12..16 and every T >= 19.
