@@ -743,7 +743,8 @@ void decode_multi_kernel(const Ptrs p, const int units, const int T)
 // which is the token-by-token step (fade, predict, correct, write, read)
 // unrolled over the chunk.  The two state products, X = C^T S for the 16
 // vectors C = (P_t z_k,t | P_t z_q,t) and the rank-8 write, run on the f32
-// matrix cores (v_mfma_f32_16x16x4f32) straight from the state registers;
+// matrix cores (v_mfma_f32_16x16x4f32) straight from the state registers
+// (X of a bf16 state's single chunk on the bf16 ones, see PackedRegs);
 // the 8 x 8 pair sums are sums over the channels, and the triangular solve
 // runs per value column.  z_k, z_q are the conv outputs before the L2 norms
 // (k^ = rk z_k, q^ = rq z_q), so the norms scale the small sums instead of
