@@ -45,8 +45,10 @@ namespace kda {
 // RMAP    0: a workgroup access covers consecutive rows (waves side by side);
 //         1: each wave owns a contiguous band of rows
 // FUSED   true: conv prologue from bf16 x + conv state; false: f32 q|k|v input
-// XG      keep the NSPLIT workgroups of a head on one XCD (they read the same
-//         q/k inputs, which then come from that XCD's L2)
+// XG      XCD-aware workgroup order: keep the NSPLIT workgroups of a head on
+//         one XCD (they read the same q/k inputs, which then come from that
+//         XCD's L2); with whole heads, alternate consecutive workgroups
+//         between the two halves of the heads (block_unit)
 // WT      state stores with agent scope as well as non-temporal (store_sc1)
 template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP>
 struct Geo {
@@ -80,8 +82,23 @@ struct Geo {
 // consecutive workgroups.  XG: workgroups are handed to the 8 XCDs round
 // robin, so within each run of 8*NSPLIT workgroups, those on one XCD are the
 // NSPLIT splits of one unit; a ragged tail of units falls back to plain.
+// XG with whole heads (NSPLIT 1): consecutive workgroups alternate between
+// the two halves of the heads (b -> (b mod 2) units/2 + b/2), so the even
+// XCDs stream the first half of the states and the odd ones the second.
+// Measured on MI355X for the 16-wave f32 grid (34 layers, us per layer,
+// plain / alternating): M = 32 47.8 / 46.4, M = 48 72.1 / 69.9, M = 64
+// 94.5 / 91.1, M = 128 186.0 / 176.1; with the states placed 3 GB further
+// into memory M = 32 47.1 / 46.8.  The 4-wave grids (bf16; one round of f32)
+// and XCD-contiguous heads (each XCD an eighth of the states) are slower.
 template <int NSPLIT, bool XG>
 __device__ __forceinline__ void block_unit(int b, int units, int& unit, int& split) {
+    if constexpr (XG && NSPLIT == 1) {
+        if ((units & 1) == 0) {
+            unit = (b & 1) * (units >> 1) + (b >> 1);
+            split = 0;
+            return;
+        }
+    }
     if constexpr (XG && NSPLIT > 1) {
         constexpr int GB = 8 * NSPLIT;
         const int full = units >> 3;
@@ -1310,7 +1327,7 @@ template <bool FUSED, int MODE>
 static hipError_t dispatch_wide_f32(const StepArgs& a) {
     if (a.nsplit == 1) {
         const long heads = (long)a.M * a.H;
-        if (heads >= 2048) return launch_decode<float, 128, 1, 16, 4, FUSED, false, 0, MODE, true>(a);
+        if (heads >= 2048) return launch_decode<float, 128, 1, 16, 4, FUSED, true, 0, MODE, true>(a);
         if (heads >= 256 && heads <= 768) return launch_decode<float, 128, 1, 4, 4, FUSED, false, 1, MODE>(a);
         return launch_decode<float, 128, 1, 8, 4, FUSED, false, 0, MODE>(a);
     }
