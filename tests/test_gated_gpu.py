@@ -123,18 +123,20 @@ def test_gated_split_path(orc, state_dtype):
 
 
 @pytest.mark.parametrize("layer_step", [False, True], ids=["gated", "layer"])
-@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-def test_gated_wide_grid(orc, state_dtype, layer_step):
+@pytest.mark.parametrize("state_dtype,M,H", [("f32", 33, 64), ("bf16", 33, 64), ("f32", 33, 63)])
+def test_gated_wide_grid(orc, state_dtype, layer_step, M, H):
     """33 x 64 = 2112 heads, whole tensors: the launches that store the state
     with agent scope (from 2048 heads on), with a partial last round of
-    workgroups."""
-    wl = kda_synth.custom("gated_wide", 33, 64, 128, steps=2)
+    workgroups.  For an f32 state also 33 x 63 = 2079 heads: the 16-wave
+    grid alternates between the two halves of the heads only when their
+    number is even, and runs them in order otherwise."""
+    wl = kda_synth.custom("gated_wide", M, H, 128, steps=2)
     lay = GatedLayer(wl, 0, state_dtype)
     S_ref, cs_ref = host(lay.state), host(lay.conv)
     for t in range(wl.steps):
         S_ref, cs_ref, e = check_step(orc, lay, S_ref, cs_ref, t, KDA_GATE_BOUNDED, -5.0, layer_step,
                                       teacher=state_dtype == "bf16")
-    say(f"{'layer' if layer_step else 'gated'} wide {state_dtype}: out {e[0]:.3e} state {e[1]:.3e}")
+    say(f"{'layer' if layer_step else 'gated'} wide {M}x{H} {state_dtype}: out {e[0]:.3e} state {e[1]:.3e}")
 
 
 def test_layer_step_glm_m32_sampled(orc):

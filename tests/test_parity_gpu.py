@@ -230,20 +230,24 @@ def test_many_units_ragged(orc, state_dtype, inplace):
     say(f"many units {state_dtype} inplace={inplace}: o {e[0]:.3e} state {e[1]:.3e}")
 
 
+@pytest.mark.parametrize("M,H", [(33, 64), (33, 63)])
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-def test_wide_grid_whole_tensors(orc, state_dtype):
-    """33 x 64 = 2112 heads, whole tensors: from 2048 heads on, the whole-head
-    launches store the state through agent-scope buffer stores instead of
-    global stores, and 2112 is not a multiple of the CU count, so the last
-    round of workgroups is partial."""
-    wl = kda_synth.custom("wide", 33, 64, 128, steps=2)
+def test_wide_grid_whole_tensors(orc, state_dtype, M, H):
+    """33 x 64 = 2112 and 33 x 63 = 2079 heads, whole tensors: from 2048 heads
+    on, the whole-head launches store the state through agent-scope buffer
+    stores instead of global stores, and neither count is a multiple of the
+    CU count, so the last round of workgroups is partial.  The 16-wave f32
+    grid takes consecutive workgroups alternately from the two halves of the
+    heads when their number is even (2112) and in order when it is odd
+    (2079); every head must be updated exactly once either way."""
+    wl = kda_synth.custom("wide", M, H, 128, steps=2)
     lay = Layer(wl, 0, DEV, state_dtype)
     S_ref, cs_ref = host(lay.state), host(lay.conv)
     for t in range(wl.steps):
         S_ref, cs_ref, e = full_step_check(orc, lay, S_ref, cs_ref,
                                            kda_synth.step_inputs(wl, 0, t, DEV), tol_state(state_dtype),
                                            teacher=state_dtype == "bf16")
-    say(f"wide grid {state_dtype}: o {e[0]:.3e} state {e[1]:.3e}")
+    say(f"wide grid {M}x{H} {state_dtype}: o {e[0]:.3e} state {e[1]:.3e}")
 
 
 def test_empty_batch():
