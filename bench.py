@@ -78,6 +78,7 @@ MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X dense FP32 matrix
 # the T-token shapes of kda_decode_multi, for the chunked path
 PREFILL_SHAPES = ((8, 2048, "f32"), (1, 8192, "f32"), (2, 4096, "f32"), (1, 4096, "bf16"), (32, 1024, "bf16"),
                   (32, 8, "f32"), (32, 16, "f32"))
+PREFILL_WARM_S = 0.1              # least time of back-to-back warm-up launches per prefill line
 
 
 def log(msg):
@@ -385,8 +386,18 @@ def measure_prefill(M, L, state_dtype, steps, warmup, H=64, D=128):
             raise RuntimeError(f"kda_prefill_gated_ws returned {rc}")
 
     with torch.cuda.stream(stream):
-        for _ in range(warmup):
+        # at least `warmup` launches and PREFILL_WARM_S seconds of back-to-back
+        # launches: the compute-bound chunk loop runs up to 10% slower until
+        # the clock has settled under load (2 launches: 1.41-1.50 ms at
+        # 8 x 2048, 20 or more: 1.35 ms; the memory-bound decode is the same
+        # after 10 or 300 warm-up steps)
+        t_warm = time.perf_counter()
+        n_warm = 0
+        while n_warm < warmup or time.perf_counter() - t_warm < PREFILL_WARM_S:
             launch()
+            n_warm += 1
+            if n_warm % 4 == 0:
+                stream.synchronize()
         stream.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record(stream)
