@@ -229,20 +229,6 @@ template <> struct Chunk<uint16_t, 4> {
     }
 };
 
-// e^x from the hardware 2^x (v_exp_f32) with the argument split into
-// x log2(e) rounded plus its rounding error, which the result then absorbs
-// to first order: within 1.3 ulp of e^x over [-87, 88] (measured against
-// double on gfx950; the libm expf: 0.84 ulp), 5 instructions instead of
-// ~13.  Flushes to 0 below about -87.3; +inf above about 88.7.
-__device__ __forceinline__ float exp_fast(float x) {
-    const float L2E = 1.44269502162933349609375f;          // log2(e) rounded to f32
-    const float L2E_LO = 1.925963033500011079e-8f;         // log2(e) - L2E
-    const float hi = x * L2E;
-    const float lo = fmaf(x, L2E, -hi) + x * L2E_LO;
-    const float r = __builtin_amdgcn_exp2f(hi);
-    return fmaf(r, lo * 0.693147180559945309f, r);
-}
-
 // Short causal conv (kernel 4) + SiLU for one channel, "GLM-5.3 deep dive"
 // 8.2.4 step 2.  w4 packs the channel's 4 bf16 taps (tap 3 = current token).
 __device__ __forceinline__ float conv_silu(u32x2 w4, float t0, float t1, float t2, float xc) {

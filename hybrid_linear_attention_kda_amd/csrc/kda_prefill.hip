@@ -99,6 +99,7 @@ struct PrefillSmem {
         u32x4 dp[3][4][2][2][16];  // Delta pieces [piece][wave][tile][token half][column]: 8 tokens each
     };
     u32x4 gqp[2][4][64];           // (Gamma . q^) pieces 1, 2 [piece][32-row block][lane]: A operand of (Gamma . Q) S
+    u32x4 wpk[4][3][64];           // -W pieces [32-row block][piece][lane]: A operand of W S, split once per chunk
     u32x4 ktp[3][8][2][16];        // ((gamma_C / Gamma) . k^) pieces [piece][row tile][token half][row]
     float Z[2][PC][LT];            // Z[j][i] = sum_c (Gamma . k^)[i][c] (k^ / Gamma)[j][c], per channel half
     float P[2][PC][LT];            // Tril((Gamma . q^)(k^ / Gamma)^T), row = query token, per channel half
@@ -127,6 +128,18 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 
 // two f32 -> packed bf16, a in the low half
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) { return pack_bf16x2(a, b); }
+
+// e^x from the hardware 2^x (v_exp_f32) of the rounded product x log2(e).
+// Rounding the product (and log2(e)) moves the result by at most about
+// 8e-8 |x| relative: 4e-7 for a decay exponent in [-5, 0], 1.3e-6 for a
+// SiLU argument of 16.  Within a chunk the decays multiply up over at most
+// 16 tokens, and a decay's error only matters in proportion to what it
+// decays, so the state moves by far less than its f32 tolerance (the
+// state and output errors against the oracle are unchanged to four
+// digits).  Sigmoid and SiLU take the hardware reciprocal as well.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(1.44269502162933349609375f * x); }
+__device__ __forceinline__ float sigmoid_hw(float y) { return __builtin_amdgcn_rcpf(1.0f + exp_hw(-y)); }
+__device__ __forceinline__ float silu_hw(float y) { return y * sigmoid_hw(y); }
 
 // the three bf16 pieces of (a, b), one packed dword each
 __device__ __forceinline__ void split2(float a, float b, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
@@ -321,7 +334,8 @@ void prefill_kernel(const Ptrs p, const int L)
         // ---- 1. inputs ----
         if (qk) {
             // tokens past the end give 0 (the carried taps are then stale,
-            // but only the last chunk has such tokens)
+            // but only the last chunk has such tokens); SiLU(0) = 0, so the
+            // argument is masked rather than the result (no branch)
             float z0[PC], z1[PC];
 #pragma unroll
             for (int j = 0; j < PC; ++j) {
@@ -334,9 +348,8 @@ void prefill_kernel(const Ptrs p, const int L)
                 y1 = fmaf(cw[5], b1, y1);
                 y1 = fmaf(cw[6], b2, y1);
                 y1 = fmaf(cw[7], x1, y1);
-                // SiLU with the hardware reciprocal (within 3.6 ulp)
-                z0[j] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
-                z1[j] = j < n ? y1 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y1)) : 0.f;
+                z0[j] = silu_hw(j < n ? y0 : 0.f);
+                z1[j] = silu_hw(j < n ? y1 : 0.f);
                 a0 = a1; a1 = a2; a2 = x0;
                 b0 = b1; b1 = b2; b2 = x1;
             }
@@ -364,16 +377,16 @@ void prefill_kernel(const Ptrs p, const int L)
                 y0 = fmaf(cw[1], a1, y0);
                 y0 = fmaf(cw[2], a2, y0);
                 y0 = fmaf(cw[3], x0, y0);
-                sm.vv[j][vc] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
+                sm.vv[j][vc] = silu_hw(j < n ? y0 : 0.f);
                 a0 = a1; a1 = a2; a2 = x0;
-                const float g = lb * __builtin_amdgcn_rcpf(1.0f + exp_fast(-eA * (bf16_lo(rawf[j]) + db)));
-                e *= j < n ? exp_fast(g) : 1.f;
+                const float g = lb * sigmoid_hw(eA * (bf16_lo(rawf[j]) + db));
+                e *= exp_hw(j < n ? g : 0.f);
                 sm.eg[j][vc] = e;
                 sm.qi[1][j][vc] = __builtin_amdgcn_rcpf(e);
             }
             sm.gam[vc] = e;
             if (wv == 3 && lane < PC)
-                sm.beta[lane] = lane < n ? __builtin_amdgcn_rcpf(1.0f + exp_fast(-bf16_lo(rawb))) : 0.0f;
+                sm.beta[lane] = lane < n ? sigmoid_hw(bf16_lo(rawb)) : 0.0f;
         }
         if (t0 + PC < L) fetch(t0 + PC);
         lds_barrier();
@@ -468,6 +481,15 @@ void prefill_kernel(const Ptrs p, const int L)
         // of token lane % 16 at the same rows) come split from LDS.  Six bf16
         // products per pair of split operands for W S (the state's path),
         // the first three of them for (Gamma . Q) S (the output's).
+        // -W is split once: wave w splits 32-row block w for every wave (the
+        // barrier below waits for all four blocks behind the split of the
+        // state's block 0, which needs no LDS).
+        {
+            u32x4 wq[3];
+            split8(lds4(&sm.kh[l16][32 * wv + 4 * g4]), lds4(&sm.kh[l16][32 * wv + 16 + 4 * g4]), wq);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) sm.wpk[wv][q][lane] = wq[q];
+        }
         f32x4 dacc[NTW], oacc[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
@@ -483,7 +505,9 @@ void prefill_kernel(const Ptrs p, const int L)
                 split8(f32x4{S[2 * kb][nt][0], S[2 * kb][nt][1], S[2 * kb][nt][2], S[2 * kb][nt][3]},
                        f32x4{S[2 * kb + 1][nt][0], S[2 * kb + 1][nt][1], S[2 * kb + 1][nt][2], S[2 * kb + 1][nt][3]},
                        sb[nt]);
-            split8(lds4(&sm.kh[l16][32 * kb + 4 * g4]), lds4(&sm.kh[l16][32 * kb + 16 + 4 * g4]), wp);   // -W
+            if (kb == 0) lds_barrier();
+#pragma unroll
+            for (int q = 0; q < 3; ++q) wp[q] = sm.wpk[kb][q][lane];                                  // -W
 #pragma unroll
             for (int q = 0; q < 2; ++q) gp[q] = sm.gqp[q][kb][lane];
 #pragma unroll
@@ -744,8 +768,8 @@ void prep_kernel(const Ptrs p, const int L, const int M, const int c0, const int
                 y1 = fmaf(cw[5], b1, y1);
                 y1 = fmaf(cw[6], b2, y1);
                 y1 = fmaf(cw[7], x1, y1);
-                z0[j] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
-                z1[j] = j < n ? y1 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y1)) : 0.f;
+                z0[j] = silu_hw(j < n ? y0 : 0.f);
+                z1[j] = silu_hw(j < n ? y1 : 0.f);
                 a0 = a1; a1 = a2; a2 = x0;
                 b0 = b1; b1 = b2; b2 = x1;
             }
@@ -769,16 +793,16 @@ void prep_kernel(const Ptrs p, const int L, const int M, const int c0, const int
                 y0 = fmaf(cw[1], a1, y0);
                 y0 = fmaf(cw[2], a2, y0);
                 y0 = fmaf(cw[3], x0, y0);
-                sm.vv[j][vc] = j < n ? y0 * __builtin_amdgcn_rcpf(1.0f + exp_fast(-y0)) : 0.f;
+                sm.vv[j][vc] = silu_hw(j < n ? y0 : 0.f);
                 a0 = a1; a1 = a2; a2 = x0;
-                const float g = lb * __builtin_amdgcn_rcpf(1.0f + exp_fast(-eA * (bf16_lo(rawf[j]) + db)));
-                e *= j < n ? exp_fast(g) : 1.f;
+                const float g = lb * sigmoid_hw(eA * (bf16_lo(rawf[j]) + db));
+                e *= exp_hw(j < n ? g : 0.f);
                 sm.eg[j][vc] = e;
                 sm.qi[1][j][vc] = __builtin_amdgcn_rcpf(e);
             }
             sm.gam[vc] = e;
             if (wv == 3 && lane < PC)
-                sm.beta[lane] = lane < n ? __builtin_amdgcn_rcpf(1.0f + exp_fast(-bf16_lo(rawb))) : 0.0f;
+                sm.beta[lane] = lane < n ? sigmoid_hw(bf16_lo(rawb)) : 0.0f;
         }
         if (cl + 1 < cl1) fetch(t0 + PC);
         lds_barrier();
