@@ -453,6 +453,13 @@ void prefill_kernel(const Ptrs p, const int L)
         }
         lds_barrier();
 
+        // Wave priority: the two workgroups on a CU drift out of step, and the
+        // phases on the serial path of a chunk go first -- the solves (a
+        // 16-step chain of readlane and FMA per column) highest, the state
+        // products and the update next -- so that the other workgroup's
+        // vector-bound inputs, A and P fill their gaps rather than delay them
+        // (8 x 2048 f32: 1.23 -> 1.10 ms per layer).
+        __builtin_amdgcn_s_setprio(2);
         // ---- 3. (I + A) W = Diag(beta)(Gamma . K), (I + A) U = Diag(beta) V ----
         // Waves 0, 1 solve for W (stored negated), waves 2, 3 for U.
         {
@@ -475,6 +482,7 @@ void prefill_kernel(const Ptrs p, const int L)
         lds_barrier();
 
         // ---- 4. Delta = U - W S and (Gamma . Q) S, this wave's 32 value columns ----
+        __builtin_amdgcn_s_setprio(1);
         // Per 32-row block of the state: the lane's 8 state values of each
         // column tile (rows 32 kb + 4 (lane / 16) + {0..3, 16..19}: its own
         // registers) are the B fragment; the A fragments (-W and Gamma . q^
@@ -586,6 +594,7 @@ void prefill_kernel(const Ptrs p, const int L)
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // the next chunk's inputs overwrite every array above
         lds_barrier();
     }
