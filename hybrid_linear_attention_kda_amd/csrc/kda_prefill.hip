@@ -328,6 +328,7 @@ void prefill_kernel(const Ptrs p, const int L)
     };
     fetch(0);
 
+    const bool prio = L > 4 * PC;
     for (int t0 = 0; t0 < L; t0 += PC) {
         const int n = min(PC, L - t0);
 
@@ -458,8 +459,11 @@ void prefill_kernel(const Ptrs p, const int L)
         // 16-step chain of readlane and FMA per column) highest, the state
         // products and the update next -- so that the other workgroup's
         // vector-bound inputs, A and P fill their gaps rather than delay them
-        // (8 x 2048 f32: 1.23 -> 1.10 ms per layer).
-        __builtin_amdgcn_s_setprio(2);
+        // (8 x 2048 f32: 1.23 -> 1.10 ms per layer).  Only for sequences of
+        // more than 4 chunks: with fewer, the state's load and store, which
+        // run at the base priority, are a large part of a workgroup's life,
+        // and delaying them costs more (32 x 16 f32: 69 -> 75 us).
+        if (prio) __builtin_amdgcn_s_setprio(2);
         // ---- 3. (I + A) W = Diag(beta)(Gamma . K), (I + A) U = Diag(beta) V ----
         // Waves 0, 1 solve for W (stored negated), waves 2, 3 for U.
         {
@@ -482,7 +486,7 @@ void prefill_kernel(const Ptrs p, const int L)
         lds_barrier();
 
         // ---- 4. Delta = U - W S and (Gamma . Q) S, this wave's 32 value columns ----
-        __builtin_amdgcn_s_setprio(1);
+        if (prio) __builtin_amdgcn_s_setprio(1);
         // Per 32-row block of the state: the lane's 8 state values of each
         // column tile (rows 32 kb + 4 (lane / 16) + {0..3, 16..19}: its own
         // registers) are the B fragment; the A fragments (-W and Gamma . q^
