@@ -26,23 +26,29 @@
 // state values (row k = 16 mt + 4 (lane / 16) + r, column n = 32 w + 16 nt +
 // lane % 16).  Per chunk, five phases:
 //
-//   1. inputs: waves 0, 1, 2 run the conv + SiLU of q, k, v (each lane two
+//   1. inputs: waves 0, 1 run the conv + SiLU of q and k (each lane two
 //      channels over the chunk's 16 tokens, the three previous raw inputs
 //      carried in registers from chunk to chunk) and the L2 norms (one
-//      transposing reduction over the wave for all 16 tokens); wave 3 runs
-//      the forget gate, its running decay product and the write strengths.
-//      The raw inputs of the next chunk are then requested, so their HBM
-//      latency hides behind phases 2 to 5.
+//      transposing reduction over the wave for all 16 tokens); waves 2, 3
+//      each take half of the channels of v and of the forget gate with its
+//      running decay product, and wave 3 the write strengths.  The raw
+//      inputs of the next chunk are then requested, so their HBM latency
+//      hides behind phases 2 to 5.
 //   2. A (waves 0, 1) and P (waves 2, 3) as 16 x 16 products, each wave
 //      over one half of the 128 channels (f32 MFMA; the halves are added
 //      where A and P are read); then all waves split Gamma . Q and
 //      (gamma_C / Gamma) . K into bf16 pieces, in MFMA fragment order.
 //   3. the triangular solves for W and U, right-looking, one column per
 //      thread (256 columns), straight from (I + A) W = Diag(beta)(Gamma . K).
-//   4. Delta = U - W S and (Gamma . Q) S; each wave needs only its own
-//      columns of Delta afterwards, so no workgroup barrier separates it
-//      from phase 5.
+//   4. Delta = U - W S and (Gamma . Q) S (-W split into its bf16 pieces
+//      once, a quarter by each wave); each wave needs only its own columns
+//      of Delta afterwards, so no workgroup barrier separates it from
+//      phase 5.
 //   5. O = (Gamma . Q) S + P Delta, stored; S' = Diag(gamma_C) S + ...
+//
+// Phases 3 to 5 are the chunk's serial path; on sequences of more than four
+// chunks they run at a raised wave priority, so that the other workgroup
+// on the CU fills their gaps with its vector-bound phases 1 and 2.
 //
 // The three state products (phases 4 and 5) run on the bf16 matrix cores
 // from three-way bf16 splits of both operands, six piece pairs per product,
