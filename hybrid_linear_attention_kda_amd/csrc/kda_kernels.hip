@@ -976,6 +976,15 @@ struct F32Regs {
     __device__ __forceinline__ void set(int mb, int r, float x0, float x1) { v[mb][r][0] = x0; v[mb][r][1] = x1; }
     template <typename TS>
     __device__ __forceinline__ void store(TS* p, int mb, int r) const { WyIO<TS>::store(p, v[mb][r][0], v[mb][r][1]); }
+    // at byte offset off of a stream_rsrc buffer, agent scope + non-temporal
+    template <typename TS>
+    __device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t rs, int off, int mb, int r) const {
+        if constexpr (sizeof(TS) == 4)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v[mb][r][0]), __float_as_uint(v[mb][r][1])},
+                                                  rs, off, 0, kCpolSc1Nt);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[mb][r][0], v[mb][r][1]), rs, off, 0, kCpolSc1Nt);
+    }
 };
 struct PackedRegs {
     static constexpr bool XB = true;
@@ -986,6 +995,10 @@ struct PackedRegs {
     __device__ __forceinline__ void set(int mb, int r, float x0, float x1) { v[mb][r] = pack_bf16x2(x0, x1); }
     __device__ __forceinline__ void store(uint16_t* p, int mb, int r) const {
         __builtin_nontemporal_store(v[mb][r], reinterpret_cast<uint32_t*>(p));
+    }
+    template <typename TS>
+    __device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t rs, int off, int mb, int r) const {
+        __builtin_amdgcn_raw_buffer_store_b32(v[mb][r], rs, off, 0, kCpolSc1Nt);
     }
     // B fragment of 32-row block j, column c: k slot i of lane group g is row
     // 32 j + 16 (i / 4) + 4 g + i % 4, two bf16 per dword
@@ -1003,7 +1016,9 @@ struct PackedRegs {
 // (M = 32, T = 8: 58.1 against 58.6 us); bf16 after the last tile and a
 // barrier, so that the two waves whose 64-byte pieces share each 128-byte
 // line store together (M = 128, T = 8: 164.2 against 166.6 us without).
-template <typename TS, bool STORE, class SR>
+// WT: the stores with agent scope as well as non-temporal (as the one-token
+// step's WT).
+template <typename TS, bool STORE, bool WT, class SR>
 __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int h, int c0, int n, WySmem& sm) {
     using namespace wy;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -1104,14 +1119,21 @@ __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int c = 0; c < 2; ++c) e[st][c] = drow(4 * st + g, 2 * nn + c);
-    TS* so = nullptr;
+    TS* const head = static_cast<TS*>(p.state) + (size_t)(m * p.H + h) * D * D;
+    const __amdgpu_buffer_rsrc_t rs = stream_rsrc(head, D * D * (int)sizeof(TS));
+    int lo = 0;
     if constexpr (STORE) {
-        // the lane's state addresses, formed here from a value the compiler
-        // cannot see into, so they are not kept live across the chunk
-        int lo = 32 * wv + 2 * nn + 4 * g * D;
+        // the lane's offset in the head, formed here from a value the
+        // compiler cannot see into, so its addresses are not kept live
+        // across the chunk
+        lo = 32 * wv + 2 * nn + 4 * g * D;
         asm volatile("" : "+v"(lo));
-        so = static_cast<TS*>(p.state) + (size_t)(m * p.H + h) * D * D + lo;
     }
+    auto store_row = [&](int mb, int r) {
+        const int e = lo + (16 * mb + r) * D;
+        if constexpr (WT) S.template store_sc1<TS>(rs, e * (int)sizeof(TS), mb, r);
+        else S.store(head + e, mb, r);
+    };
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
         const f32x4 gd = *reinterpret_cast<const f32x4*>(&sm.G[16 * mb + 4 * g]);
@@ -1128,7 +1150,7 @@ __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int
         for (int r = 0; r < 4; ++r) S.set(mb, r, cv[0][r], cv[1][r]);
         if constexpr (STORE && sizeof(TS) == 4) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S.store(so + (size_t)(16 * mb + r) * D, mb, r);
+            for (int r = 0; r < 4; ++r) store_row(mb, r);
         }
     }
     if constexpr (STORE && sizeof(TS) == 2) {
@@ -1136,7 +1158,7 @@ __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S.store(so + (size_t)(16 * mb + r) * D, mb, r);
+            for (int r = 0; r < 4; ++r) store_row(mb, r);
     }
     // the next chunk overwrites the inputs, X, delta, C, K and G
     if constexpr (!STORE) lds_barrier();
@@ -1146,8 +1168,9 @@ __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int
 // right behind the chunk's input loads and the second once their registers
 // are free, so the state streams in while the inputs wait and the
 // coefficients are formed.  Otherwise chunk after chunk, the state requested
-// once the first chunk's coefficients are formed.
-template <typename TS, bool ONE>
+// once the first chunk's coefficients are formed.  WT: the state stores
+// with agent scope as well (grids of several rounds of workgroups).
+template <typename TS, bool ONE, bool WT>
 __global__ __launch_bounds__(wy::NT, 4)
 void decode_wy_kernel(const Ptrs p, const int units, const int T)
 {
@@ -1184,7 +1207,7 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
             for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S.v[mb][r][0], S.v[mb][r][1]);
-            wy_chunk<TS, true>(S, p, T, m, h, 0, T, sm);
+            wy_chunk<TS, true, WT>(S, p, T, m, h, 0, T, sm);
         } else {
             wy_coeffs<true>(T, sm);
             lds_barrier();
@@ -1193,7 +1216,7 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
             for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S.v[mb][r] = raw[mb][r];
-            wy_chunk<TS, true>(S, p, T, m, h, 0, T, sm);
+            wy_chunk<TS, true, WT>(S, p, T, m, h, 0, T, sm);
         }
     } else {
         F32Regs S;
@@ -1213,21 +1236,26 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) IO::unpack(raw[mb][r], S.v[mb][r][0], S.v[mb][r][1]);
-        wy_chunk<TS, false>(S, p, T, m, h, 0, n, sm);
+        wy_chunk<TS, false, false>(S, p, T, m, h, 0, n, sm);
         for (int c0 = TC; c0 < T; c0 += TC) {
             const int n2 = min(TC, T - c0);
             multi_chunk<MG, D, false, WySmem>(p, T, m, h, c0, n2, sm);   // item by item beside the state
             wy_coeffs(n2, sm);
             lds_barrier();
-            wy_chunk<TS, false>(S, p, T, m, h, c0, n2, sm);
+            wy_chunk<TS, false, false>(S, p, T, m, h, c0, n2, sm);
         }
         int lo = 32 * wv + 2 * nn + 4 * g * D;
         asm volatile("" : "+v"(lo));
-        TS* const so = static_cast<TS*>(p.state) + (size_t)unit * D * D + lo;
+        TS* const head = static_cast<TS*>(p.state) + (size_t)unit * D * D;
+        const __amdgpu_buffer_rsrc_t rs = stream_rsrc(head, D * D * (int)sizeof(TS));
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) IO::store(so + (size_t)(16 * mb + r) * D, S.v[mb][r][0], S.v[mb][r][1]);
+            for (int r = 0; r < 4; ++r) {
+                const int e = lo + (16 * mb + r) * D;
+                if constexpr (WT) S.template store_sc1<TS>(rs, e * (int)sizeof(TS), mb, r);
+                else IO::store(head + e, S.v[mb][r][0], S.v[mb][r][1]);
+            }
     }
 
     if (tid < MG::NGT) {
@@ -1387,8 +1415,13 @@ static hipError_t launch_wy(const StepArgs& a) {
     int units = a.M * a.H;
     int T = a.T;
     void* args[] = {(void*)&p, (void*)&units, (void*)&T};
-    const void* fn = T <= wy::TC ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, true>)
-                                 : reinterpret_cast<const void*>(&decode_wy_kernel<TS, false>);
+    // agent-scope stores from 2048 heads on, as the one-token step (M = 128
+    // bf16, T = 8: 154.6 -> 149.1 us; M = 32 f32 unchanged)
+    const bool wt = units >= 2048;
+    const void* fn = T <= wy::TC ? (wt ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, true, true>)
+                                       : reinterpret_cast<const void*>(&decode_wy_kernel<TS, true, false>))
+                                 : (wt ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, false, true>)
+                                       : reinterpret_cast<const void*>(&decode_wy_kernel<TS, false, false>));
     return hipLaunchKernel(fn, dim3((unsigned)units), dim3(wy::NT), args, 0, (hipStream_t)a.stream);
 }
 

@@ -86,6 +86,24 @@ def test_multi_equals_single_steps_f32(M, H, D, T):
     assert rel_err(host(S), host(S2)) <= 2e-6
 
 
+@pytest.mark.parametrize("state_dtype,T", [("f32", 8), ("bf16", 8), ("f32", 12), ("bf16", 20)])
+def test_multi_wide_grid_whole_tensors(orc, state_dtype, T):
+    """33 x 64 = 2112 heads, whole tensors: from 2048 heads on the chunk form
+    stores the state with agent scope (buffer stores over each head's
+    bytes), both in the one-chunk launch (T = 8) and after the chunk loop
+    (T = 12, 20); 2112 is not a multiple of the CU count."""
+    wl = kda_synth.custom("multi_wide", 33, 64, 128, steps=T)
+    S0, cs0, li, ins, S, cout, o = run_multi(wl, state_dtype, T, False)
+    S_ref, cs_ref, o_ref = orc.decode_multi(S0, host(ins["x"]), host(li["conv_w"]), cs0,
+                                            host(ins["alpha"]), host(ins["beta"]), wl.scale)
+    assert np.array_equal(host(cout), cs_ref), "conv state after T tokens"
+    e_s = rel_err(host(S), S_ref)
+    e_o = max(rel_err(host(o[:, t]), o_ref[:, t]) for t in range(T))
+    say(f"multi wide T={T} {state_dtype}: state {e_s:.3e} o {e_o:.3e}")
+    assert e_s <= tol_state(state_dtype), f"state error {e_s:.3e}"
+    assert e_o <= TOL_O, f"output error {e_o:.3e}"
+
+
 def test_multi_glm_m32_sampled(orc):
     """The benchmark's multi-token launch (M = 32, T = 8, FP32 state) on
     sampled (stream, head) units against the oracle."""
