@@ -796,7 +796,11 @@ struct WySmem {
         // the same as three bf16 pieces (bf16 state, one chunk), [piece][vector][row slot]
         __attribute__((aligned(16))) uint16_t Cb[3][16][wy::CBS];
     };
-    __attribute__((aligned(16))) float K[wy::TC][wy::KS];      // A operand of the write: g(n-1,s) z_k,s
+    union {
+        __attribute__((aligned(16))) float K[wy::TC][wy::KS];  // A operand of the write: g(n-1,s) z_k,s
+        // the same as two bf16 pieces (bf16 state, one chunk), [piece][row]: a row's 8 tokens
+        u32x4 Kp[2][wy::D];
+    };
     __attribute__((aligned(16))) float G[wy::D];               // P_{n-1}
     float red[4][2][16];                                       // pair sums per wave (64 channels each)
 };
@@ -948,11 +952,26 @@ __device__ __forceinline__ void wy_coeffs(int n, WySmem& sm) {
             row[3] = f32x4{cq[4], cq[5], cq[6], cq[7]};
         }
     } else {
-        float suf = 1.0f;
+        float suf = 1.0f, kv[TC];
 #pragma unroll
         for (int s = TC - 1; s >= 0; --s) {
-            sm.K[s][c] = suf * zk[s];              // 0 past the chunk's last token
+            kv[s] = suf * zk[s];                   // 0 past the chunk's last token
             if (s < n) suf *= av[s];
+        }
+        if constexpr (XB) {
+            // two bf16 pieces per value (the second the nearest bf16 of the
+            // remainder: the pair carries 16 bits), row c's tokens in order
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                hi[q] = pack_bf16x2(kv[2 * q], kv[2 * q + 1]);
+                lo[q] = pack_bf16x2(kv[2 * q] - bf16_lo(hi[q]), kv[2 * q + 1] - bf16_hi(hi[q]));
+            }
+            sm.Kp[0][c] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            sm.Kp[1][c] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        } else {
+#pragma unroll
+            for (int s = 0; s < TC; ++s) sm.K[s][c] = kv[s];
         }
         sm.G[c] = suf;                             // prod of a_0 .. a_{n-1}
     }
@@ -1114,11 +1133,33 @@ __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int
     __builtin_amdgcn_wave_barrier();
 
     // ---- S <- Diag(G) S + K^T E on the matrix cores ----
+    // f32 registers: two v_mfma_f32_16x16x4f32 per tile over the 8 tokens.
+    // Packed bf16 registers (the state is rounded to bf16 after the write):
+    // one v_mfma_f32_16x16x32_bf16 per tile whose k slots hold K_hi E_hi,
+    // K_hi E_lo, K_lo E_hi (8 tokens each) and zeros, the two-piece operands
+    // carrying 16 bits: the update's error stays about 2^-16 of it, far
+    // below the state's final rounding.
     float e[2][2];
+    u32x4 eb[2];
+    if constexpr (SR::XB) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+        for (int c = 0; c < 2; ++c) {
+            uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) e[st][c] = drow(4 * st + g, 2 * nn + c);
+            for (int q = 0; q < 4; ++q) {
+                const float e0 = drow(2 * q, 2 * nn + c), e1 = drow(2 * q + 1, 2 * nn + c);
+                hi[q] = pack_bf16x2(e0, e1);
+                lo[q] = pack_bf16x2(e0 - bf16_lo(hi[q]), e1 - bf16_hi(hi[q]));
+            }
+            eb[c] = g == 1 ? u32x4{lo[0], lo[1], lo[2], lo[3]}
+                           : (g == 3 ? u32x4{0u, 0u, 0u, 0u} : u32x4{hi[0], hi[1], hi[2], hi[3]});
+        }
+    } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) e[st][c] = drow(4 * st + g, 2 * nn + c);
+    }
     TS* const head = static_cast<TS*>(p.state) + (size_t)(m * p.H + h) * D * D;
     const __amdgpu_buffer_rsrc_t rs = stream_rsrc(head, D * D * (int)sizeof(TS));
     int lo = 0;
@@ -1137,14 +1178,26 @@ __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
         const f32x4 gd = *reinterpret_cast<const f32x4*>(&sm.G[16 * mb + 4 * g]);
-        const float k0 = sm.K[g][16 * mb + nn], k1 = sm.K[4 + g][16 * mb + nn];
         f32x4 cv[2];
+        if constexpr (SR::XB) {
+            typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+            const u32x4 ka = g == 3 ? u32x4{0u, 0u, 0u, 0u} : sm.Kp[g == 2][16 * mb + nn];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            cv[c] = f32x4{S.get(mb, 0, c) * gd[0], S.get(mb, 1, c) * gd[1], S.get(mb, 2, c) * gd[2],
-                          S.get(mb, 3, c) * gd[3]};
-            cv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(k0, e[0][c], cv[c], 0, 0, 0);
-            cv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(k1, e[1][c], cv[c], 0, 0, 0);
+            for (int c = 0; c < 2; ++c) {
+                cv[c] = f32x4{S.get(mb, 0, c) * gd[0], S.get(mb, 1, c) * gd[1], S.get(mb, 2, c) * gd[2],
+                              S.get(mb, 3, c) * gd[3]};
+                cv[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                                __builtin_bit_cast(bf16x8_t, eb[c]), cv[c], 0, 0, 0);
+            }
+        } else {
+            const float k0 = sm.K[g][16 * mb + nn], k1 = sm.K[4 + g][16 * mb + nn];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                cv[c] = f32x4{S.get(mb, 0, c) * gd[0], S.get(mb, 1, c) * gd[1], S.get(mb, 2, c) * gd[2],
+                              S.get(mb, 3, c) * gd[3]};
+                cv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(k0, e[0][c], cv[c], 0, 0, 0);
+                cv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(k1, e[1][c], cv[c], 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) S.set(mb, r, cv[0][r], cv[1][r]);
