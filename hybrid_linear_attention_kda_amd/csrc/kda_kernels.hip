@@ -1220,10 +1220,14 @@ __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int
 // ONE: T <= 8, a single chunk, its state requested in two halves, the first
 // right behind the chunk's input loads and the second once their registers
 // are free, so the state streams in while the inputs wait and the
-// coefficients are formed.  Otherwise chunk after chunk, the state requested
-// once the first chunk's coefficients are formed.  WT: the state stores
-// with agent scope as well (grids of several rounds of workgroups).
-template <typename TS, bool ONE, bool WT>
+// coefficients are formed.  With STAG (f32 only) the odd workgroups --
+// which, dealt round robin to the 8 XCDs, are those of the odd XCDs --
+// request their whole state only after forming the coefficients, so the
+// first round of workgroups does not ask for every head's state at once.
+// Otherwise chunk after chunk, the state requested once the first chunk's
+// coefficients are formed.  WT: the state stores with agent scope as well
+// (grids of several rounds of workgroups).
+template <typename TS, bool ONE, bool WT, bool STAG = false>
 __global__ __launch_bounds__(wy::NT, 4)
 void decode_wy_kernel(const Ptrs p, const int units, const int T)
 {
@@ -1247,13 +1251,20 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
                 for (int r = 0; r < 4; ++r) raw[mb][r] = IO::load(st + (size_t)(16 * mb + 4 * g + r) * D);
         };
         // (bf16: the whole state fits beside the chunk's input registers)
+        const bool late = sizeof(TS) == 4 && STAG && (blockIdx.x & 1) != 0;
         multi_chunk<MG, D, true, WySmem>(p, T, m, h, 0, T, sm, [&]() {
-            half(0);
+            if (!late) half(0);
             if constexpr (sizeof(TS) == 2) half(1);
         });
         if constexpr (sizeof(TS) == 4) {
-            half(1);
-            wy_coeffs(T, sm);
+            if (!late) {
+                half(1);
+                wy_coeffs(T, sm);
+            } else {
+                wy_coeffs(T, sm);
+                half(0);
+                half(1);
+            }
             lds_barrier();
             F32Regs S;
 #pragma unroll
@@ -1471,10 +1482,19 @@ static hipError_t launch_wy(const StepArgs& a) {
     // agent-scope stores from 2048 heads on, as the one-token step (M = 128
     // bf16, T = 8: 154.6 -> 149.1 us; M = 32 f32 unchanged)
     const bool wt = units >= 2048;
-    const void* fn = T <= wy::TC ? (wt ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, true, true>)
-                                       : reinterpret_cast<const void*>(&decode_wy_kernel<TS, true, false>))
-                                 : (wt ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, false, true>)
-                                       : reinterpret_cast<const void*>(&decode_wy_kernel<TS, false, false>));
+    // f32 single chunks of 5 to 8 tokens: the staggered form, half the
+    // workgroups requesting their state after the coefficients (one process,
+    // alternating builds, us per call, M = 32: T = 8 58.3 -> 57.6, T = 6
+    // 56.4 -> 56.1, T = 5 55.5 -> 55.3, but T = 4 54.3 -> 54.5 and T = 2
+    // 51.8 -> 53.0; M = 8: T = 8 18.6 -> 16.7, T = 6 16.9 -> 16.1)
+    const bool stag = sizeof(TS) == 4 && T >= 5;
+    const void* fn = T <= wy::TC
+        ? (stag ? (wt ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, true, true, true>)
+                      : reinterpret_cast<const void*>(&decode_wy_kernel<TS, true, false, true>))
+                : (wt ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, true, true>)
+                      : reinterpret_cast<const void*>(&decode_wy_kernel<TS, true, false>)))
+        : (wt ? reinterpret_cast<const void*>(&decode_wy_kernel<TS, false, true>)
+              : reinterpret_cast<const void*>(&decode_wy_kernel<TS, false, false>));
     return hipLaunchKernel(fn, dim3((unsigned)units), dim3(wy::NT), args, 0, (hipStream_t)a.stream);
 }
 
