@@ -439,6 +439,14 @@ __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&r
 // One workgroup per (unit, split): grid M*H*NSPLIT.  The small prologue
 // loads go first, then every state load of the lane (all in flight
 // together); the conv + SiLU runs while the state is still arriving.
+// Staggered (f32 state, WT grids: 2048 heads and more): the odd workgroups
+// -- dealt round robin to the 8 XCDs, those of the odd XCDs -- request their
+// state only after the conv, so half the grid's state requests trail the
+// other half's.  Measured (34 layers in a hipGraph, one process,
+// alternating builds, us per layer at M = 32): plain 47.25 -> 46.74-46.92,
+// gated 48.04 -> 47.06, layer 47.48 -> 47.36; odd pairs of workgroups late
+// 47.45, the first round's odd workgroups only 47.68-47.99; bf16 grids
+// (M = 128) do not gain and keep the plain order.
 template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG, int MODE, bool WT>
 __global__ __launch_bounds__(NWAVES * 64)
 void decode_kernel(const Ptrs p, const int units)
@@ -453,10 +461,13 @@ void decode_kernel(const Ptrs p, const int units)
     // the conv prologue then waits only for them, not for the state
     __builtin_amdgcn_sched_barrier(0);
     typename G::raw_t raw[G::RPL];
-    load_state<TS, G, D>(raw, p, unit, split, true);
+    constexpr bool STAG = WT && sizeof(TS) == 4;
+    const bool late = STAG && (blockIdx.x & 1) != 0;
+    if (!late) load_state<TS, G, D>(raw, p, unit, split, true);
     __builtin_amdgcn_sched_barrier(0);
     conv_unit<G, D, FUSED, MODE>(in, p, unit, split, sm);
     lds_barrier();
+    if (late) load_state<TS, G, D>(raw, p, unit, split, true);
     update_unit<TS, G, D, MODE, WT>(in, raw, p, unit, split, sm);
 }
 
