@@ -86,12 +86,14 @@ def test_multi_equals_single_steps_f32(M, H, D, T):
     assert rel_err(host(S), host(S2)) <= 2e-6
 
 
-@pytest.mark.parametrize("state_dtype,T", [("f32", 8), ("bf16", 8), ("f32", 12), ("bf16", 20)])
+@pytest.mark.parametrize("state_dtype,T", [("f32", 8), ("f32", 5), ("bf16", 8), ("f32", 12), ("bf16", 20)])
 def test_multi_wide_grid_whole_tensors(orc, state_dtype, T):
     """33 x 64 = 2112 heads, whole tensors: from 2048 heads on the chunk form
     stores the state with agent scope (buffer stores over each head's
-    bytes), both in the one-chunk launch (T = 8) and after the chunk loop
-    (T = 12, 20); 2112 is not a multiple of the CU count."""
+    bytes), both in the one-chunk launch (T = 8; f32 T = 5 and 8 in the
+    staggered form, whose odd workgroups request their state after the
+    coefficients) and after the chunk loop (T = 12, 20); 2112 is not a
+    multiple of the CU count."""
     wl = kda_synth.custom("multi_wide", 33, 64, 128, steps=T)
     S0, cs0, li, ins, S, cout, o = run_multi(wl, state_dtype, T, False)
     S_ref, cs_ref, o_ref = orc.decode_multi(S0, host(ins["x"]), host(li["conv_w"]), cs0,
