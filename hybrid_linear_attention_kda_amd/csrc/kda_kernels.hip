@@ -83,18 +83,21 @@ struct Geo {
 // robin, so within each run of 8*NSPLIT workgroups, those on one XCD are the
 // NSPLIT splits of one unit; a ragged tail of units falls back to plain.
 // XG with whole heads (NSPLIT 1): consecutive workgroups alternate between
-// the two halves of the heads (b -> (b mod 2) units/2 + b/2), so the even
-// XCDs stream the first half of the states and the odd ones the second.
-// Measured on MI355X for the 16-wave f32 grid (34 layers, us per layer,
-// plain / alternating): M = 32 47.8 / 46.4, M = 48 72.1 / 69.9, M = 64
-// 94.5 / 91.1, M = 128 186.0 / 176.1; with the states placed 3 GB further
-// into memory M = 32 47.1 / 46.8.  The 4-wave grids (bf16; one round of f32)
-// and XCD-contiguous heads (each XCD an eighth of the states) are slower.
+// the two halves of the heads, so the even XCDs stream the first half of the
+// states upwards (b -> b/2) and the odd ones the second half downwards
+// (b -> units - 1 - b/2).  Measured on MI355X for the 16-wave f32 grid (34
+// layers, us per layer, plain / alternating, both halves upwards): M = 32
+// 47.8 / 46.4, M = 48 72.1 / 69.9, M = 64 94.5 / 91.1, M = 128 186.0 /
+// 176.1; with the states placed 3 GB further into memory M = 32 47.1 /
+// 46.8.  The second half downwards, with the staggered state requests (one
+// process, alternating builds, M = 32): plain 46.9 -> 46.8, gated 47.6 ->
+// 46.9, layer 47.4 -> 47.2.  The 4-wave grids (bf16; one round of f32) and
+// XCD-contiguous heads (each XCD an eighth of the states) are slower.
 template <int NSPLIT, bool XG>
 __device__ __forceinline__ void block_unit(int b, int units, int& unit, int& split) {
     if constexpr (XG && NSPLIT == 1) {
         if ((units & 1) == 0) {
-            unit = (b & 1) * (units >> 1) + (b >> 1);
+            unit = (b & 1) ? units - 1 - (b >> 1) : (b >> 1);
             split = 0;
             return;
         }
