@@ -1238,9 +1238,13 @@ __device__ __forceinline__ void wy_chunk(SR& S, const Ptrs& p, int T, int m, int
 // which, dealt round robin to the 8 XCDs, are those of the odd XCDs --
 // request their whole state only after forming the coefficients, so the
 // first round of workgroups does not ask for every head's state at once.
-// Otherwise chunk after chunk, the state requested once the first chunk's
-// coefficients are formed.  WT: the state stores with agent scope as well
-// (grids of several rounds of workgroups).
+// f32 single chunks also take the one-token step's XCD-aware order (even
+// workgroups the first half of the heads upwards, odd ones the second half
+// downwards; one process, alternating builds, us per call: M = 32 T = 8
+// 57.3 -> 56.8, T = 6 55.8 -> 55.1, T = 4 unchanged, M = 8 T = 8 16.9 ->
+// 16.4).  Otherwise chunk after chunk, the state requested once the first
+// chunk's coefficients are formed.  WT: the state stores with agent scope as
+// well (grids of several rounds of workgroups).
 template <typename TS, bool ONE, bool WT, bool STAG = false>
 __global__ __launch_bounds__(wy::NT, 4)
 void decode_wy_kernel(const Ptrs p, const int units, const int T)
@@ -1249,7 +1253,8 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
     typedef MultiGeo<TS, D, 4, 4, 1, TC> MG;
     typedef WyIO<TS> IO;
     __shared__ WySmem sm;
-    const int unit = (int)blockIdx.x;
+    const int b = (int)blockIdx.x;
+    const int unit = sizeof(TS) == 4 && ONE && (units & 1) == 0 ? ((b & 1) ? units - 1 - (b >> 1) : (b >> 1)) : b;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 4, nn = lane & 15;
     const int m = unit / p.H, h = unit - m * p.H;
