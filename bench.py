@@ -558,11 +558,11 @@ def _counter_means(run_dir, counter):
     return {k: (v[0] / v[2], v[1] / v[2], v[2]) for k, v in acc.items()}
 
 
-def traffic_from_counters(fetch_dir, write_dir):
+def traffic_from_counters(fetch_dir, write_dir, out=TRAFFIC_FILE):
     """HBM bytes per headline decode launch from FETCH_SIZE and WRITE_SIZE,
     each scaled by what the same counter reads for the probe's in-place rmw
-    (grid size x 16 bytes read and the same written), and stored with the
-    kernel source's hash so that a later kernel change voids it."""
+    (grid size x 16 bytes read and the same written), and stored (in `out`)
+    with the kernel source's hash so that a later kernel change voids it."""
     decode_key = "decode_kernel<float, 128, 1, 16, 4"
     fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
 
@@ -592,16 +592,17 @@ def traffic_from_counters(fetch_dir, write_dir):
                         "fetch_size_kib": f_probe[0], "write_size_kib": w_probe[0],
                         "fetch_scale": k_fetch, "write_scale": k_write},
     }
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
+    return rec
 
 
-def stored_traffic(alg_bytes):
+def stored_traffic(path=TRAFFIC_FILE):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
     if the kernel source changed since they were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -708,7 +709,7 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBS,
-        "traffic": stored_traffic(head["alg_bytes_per_launch"]),
+        "traffic": stored_traffic(),
         "kernel": "decode_kernel<float, D=128, NSPLIT=1, NWAVES=16, VEC=4>",
         "alg_bytes_per_launch": head["alg_bytes_per_launch"],
         "avg_launch_us": avg_launch_s * 1e6,
