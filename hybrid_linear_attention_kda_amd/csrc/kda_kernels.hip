@@ -22,7 +22,10 @@
 //  * Loads and stores of the state are 16 bytes per lane; a wave covers whole
 //    contiguous rows (512 B f32 / 256 B bf16), so every access is coalesced.
 //  * All state loads are issued before the conv prologue is computed; the
-//    barriers in between only fence LDS, so the loads stay in flight.
+//    barriers in between only fence LDS, so the loads stay in flight.  On
+//    f32 grids of 2048 heads and more the odd workgroups (those of the odd
+//    XCDs) issue theirs after the conv instead, so that the two XCDs of each
+//    pair request their heads' state out of phase.
 //  * Reductions over key rows: in-lane FMAs, then a butterfly across the lanes
 //    that share columns, then (NWAVES > 1) one exchange through LDS.
 
@@ -448,8 +451,10 @@ __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&r
 // other half's.  Measured (34 layers in a hipGraph, one process,
 // alternating builds, us per layer at M = 32): plain 47.25 -> 46.74-46.92,
 // gated 48.04 -> 47.06, layer 47.48 -> 47.36; odd pairs of workgroups late
-// 47.45, the first round's odd workgroups only 47.68-47.99; bf16 grids
-// (M = 128) do not gain and keep the plain order.
+// 47.45, the first round's odd workgroups only 47.68-47.99.  bf16 grids
+// (M = 32: 26.6 against 25.9 us; M = 128: 96.3 against 95.7) and the
+// single-round grids of M = 8 (f32 13.9 against 12.3) lose, so they keep
+// the plain requests.
 template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG, int MODE, bool WT>
 __global__ __launch_bounds__(NWAVES * 64)
 void decode_kernel(const Ptrs p, const int units)
