@@ -219,14 +219,14 @@ __device__ __forceinline__ float gate_alpha(float fb, float eA, int kind, float 
 // Issue every state load of this lane for unit `unit`.  live == false issues
 // the same number of loads, all from the unit's first row segment (a
 // placeholder that keeps the instruction stream, and its wait counts, fixed).
-template <typename TS, class G, int D>
+template <typename TS, class G, int D, int T0 = 0, int T1 = G::RPL>
 __device__ __forceinline__ void load_state(typename G::raw_t (&raw)[G::RPL], const Ptrs& p, int unit,
                                            int split, bool live) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int cg = lane % G::CG, rw = lane / G::CG;
     const TS* st = static_cast<const TS*>(p.state) + (size_t)unit * D * D + split * G::COLS + cg * G::IO_VEC;
 #pragma unroll
-    for (int t = 0; t < G::RPL; ++t) raw[t] = G::IO::load(st + (live ? (size_t)G::row(wv, rw, t) * D : 0));
+    for (int t = T0; t < T1; ++t) raw[t] = G::IO::load(st + (live ? (size_t)G::row(wv, rw, t) * D : 0));
 }
 
 // Conv + SiLU of one unit's channels into LDS and the conv state shift;
@@ -283,8 +283,11 @@ __device__ __forceinline__ void conv_unit(const Pro& in, const Ptrs& p, int unit
 
 // The rest of one unit, after conv_unit and a barrier: norms, fade and both
 // reductions, one cross-wave exchange, delta correction, readout, rank-1
-// write and the stores.
-template <typename TS, class G, int D, int MODE, bool WT>
+// write and the stores.  PK (bf16 state): the state stays in its packed
+// registers; the reductions and the write each unpack the rows again (the
+// same products in the same order, so the same results) instead of
+// holding them as f32 -- 64 VGPRs instead of 112, 8 workgroups per CU.
+template <typename TS, class G, int D, int MODE, bool WT, bool PK = false>
 __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&raw)[G::RPL], const Ptrs& p,
                                             int unit, int split, Smem<G, D>& sm) {
     constexpr int NT = G::NT, COLS = G::COLS, CG = G::CG, RPL = G::RPL, VEC = G::IO_VEC;
@@ -317,10 +320,29 @@ __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&r
     const float kq = sqk * rq * rk;                    // k^ . q^
 
     // ---- fade, and the two reductions over this lane's rows ----
-    float sreg[RPL][VEC], kk[RPL];
+    static_assert(!PK || sizeof(TS) == 2, "the packed form is for a bf16 state");
+    float sreg[PK ? 1 : RPL][VEC], kk[PK ? 1 : RPL];
     float u[VEC], wq[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) { u[e] = 0.0f; wq[e] = 0.0f; }
+    if constexpr (PK) {
+        // four rows between scheduling fences, so that the rows' LDS
+        // scalars are not all fetched (and held) at once
+#pragma unroll
+        for (int t = 0; t < RPL; ++t) {
+            if (t % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+            const int i = G::row(wv, rw, t);
+            const float a = sm.a[i], qq = s_q[i] * rq, k_ = s_k[i] * rk;
+            float s4[VEC];
+            G::IO::unpack(raw[t], s4);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float sv = s4[e] * a;
+                u[e] = fmaf(sv, k_, u[e]);
+                wq[e] = fmaf(sv, qq, wq[e]);
+            }
+        }
+    } else
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
         const int i = G::row(wv, rw, t);
@@ -397,6 +419,32 @@ __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&r
     // ---- rank-1 write and store ----
     TS* const st = static_cast<TS*>(p.state) + (size_t)unit * D * D;
     const auto rs = stream_rsrc(st, D * D * (int)sizeof(TS));   // used with WT only
+    if constexpr (PK) {
+        // the faded row formed again from the packed bf16 (the products
+        // the reductions used), then the rank-1 write.  The raw pairs and
+        // the store offsets' base pass through empty asm statements, so the
+        // compiler neither keeps the reductions' unpacked rows (64 VGPRs)
+        // nor the load addresses live until here.
+        int lo = G::row(wv, rw, 0) * D + col0;
+        asm volatile("" : "+v"(lo));
+#pragma unroll
+        for (int t = 0; t < RPL; ++t) asm volatile("" : "+v"(raw[t]));
+#pragma unroll
+        for (int t = 0; t < RPL; ++t) {
+            if (t % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+            const int i = G::row(wv, rw, t);
+            const float a = sm.a[i], k_ = s_k[i] * rk;
+            float s4[VEC];
+            G::IO::unpack(raw[t], s4);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s4[e] = fmaf(k_, d[e], s4[e] * a);
+            const int off = lo + (G::row(0, 0, t) - G::row(0, 0, 0)) * D;
+            if constexpr (WT)
+                G::IO::store_sc1(rs, off * (int)sizeof(TS), s4);
+            else
+                G::IO::store(st + off, s4);
+        }
+    } else
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
 #pragma unroll
@@ -455,8 +503,12 @@ __device__ __forceinline__ void update_unit(const Pro& in, typename G::raw_t (&r
 // (M = 32: 26.6 against 25.9 us; M = 128: 96.3 against 95.7) and the
 // single-round grids of M = 8 (f32 13.9 against 12.3) lose, so they keep
 // the plain requests.
-template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG, int MODE, bool WT>
-__global__ __launch_bounds__(NWAVES * 64)
+// PK (bf16 state, see update_unit): half of each lane's state loads before
+// the conv and half after it, so the conv's inputs and the state's packed
+// registers fit 64 VGPRs together (8 workgroups per CU).
+template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, int RMAP, bool FUSED, bool XG, int MODE, bool WT,
+          bool PK = false>
+__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(PK ? 8 : 1)))
 void decode_kernel(const Ptrs p, const int units)
 {
     typedef Geo<TS, D, NSPLIT, NWAVES, VEC, RMAP> G;
@@ -471,12 +523,14 @@ void decode_kernel(const Ptrs p, const int units)
     typename G::raw_t raw[G::RPL];
     constexpr bool STAG = WT && sizeof(TS) == 4;
     const bool late = STAG && (blockIdx.x & 1) != 0;
-    if (!late) load_state<TS, G, D>(raw, p, unit, split, true);
+    if constexpr (PK) load_state<TS, G, D, 0, G::RPL / 2>(raw, p, unit, split, true);
+    else if (!late) load_state<TS, G, D>(raw, p, unit, split, true);
     __builtin_amdgcn_sched_barrier(0);
     conv_unit<G, D, FUSED, MODE>(in, p, unit, split, sm);
     lds_barrier();
-    if (late) load_state<TS, G, D>(raw, p, unit, split, true);
-    update_unit<TS, G, D, MODE, WT>(in, raw, p, unit, split, sm);
+    if constexpr (PK) load_state<TS, G, D, G::RPL / 2, G::RPL>(raw, p, unit, split, true);
+    else if (late) load_state<TS, G, D>(raw, p, unit, split, true);
+    update_unit<TS, G, D, MODE, WT, PK>(in, raw, p, unit, split, sm);
 }
 
 // ------------------------------------------------------- T tokens per launch --
@@ -1402,7 +1456,7 @@ void conv_kernel(const int M, const int C, const uint16_t* __restrict__ x,
 
 
 template <typename TS, int D, int NSPLIT, int NWAVES, int VEC, bool FUSED, bool XG, int RMAP = 0, int MODE = 0,
-          bool WT = false>
+          bool WT = false, bool PK = false>
 static hipError_t launch_decode(const StepArgs& a) {
     Ptrs p = make_ptrs(a);
     int units = a.M * a.H;
@@ -1410,7 +1464,7 @@ static hipError_t launch_decode(const StepArgs& a) {
     const dim3 grid((unsigned)((long)units * NSPLIT));
     const dim3 block(NWAVES * 64);
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&decode_kernel<TS, D, NSPLIT, NWAVES, VEC, RMAP, FUSED, XG, MODE, WT>), grid,
+        reinterpret_cast<const void*>(&decode_kernel<TS, D, NSPLIT, NWAVES, VEC, RMAP, FUSED, XG, MODE, WT, PK>), grid,
         block, args, 0, (hipStream_t)a.stream);
 }
 
@@ -1456,9 +1510,22 @@ static hipError_t dispatch_wide_f32(const StepArgs& a) {
 
 template <bool FUSED, int MODE>
 static hipError_t dispatch_wide_bf16(const StepArgs& a) {
-    if (a.nsplit == 1)
-        return (long)a.M * a.H >= 2048 ? launch_decode<uint16_t, 128, 1, 4, 4, FUSED, false, 1, MODE, true>(a)
-                                       : launch_decode<uint16_t, 128, 1, 4, 4, FUSED, false, 1, MODE>(a);
+    if (a.nsplit == 1) {
+        const long heads = (long)a.M * a.H;
+        // plain step, one round of 8 packed workgroups per CU: M = 32 25.8
+        // -> 25.4 us, M = 8 7.73 -> 7.56 (one process, alternating builds);
+        // with several rounds (M = 128 95.9 -> 98.0) and for the gated and
+        // layer steps (26.1 -> 27.5 at M = 32: their gate inputs spill at
+        // 64 VGPRs) the unpacked form at 4 workgroups per CU stays
+        if constexpr (MODE == 0) {
+            const int cus = stream_cu_count(a.stream);
+            if (cus > 0 && heads <= 8L * cus)
+                return heads >= 2048 ? launch_decode<uint16_t, 128, 1, 4, 4, FUSED, false, 1, MODE, true, true>(a)
+                                     : launch_decode<uint16_t, 128, 1, 4, 4, FUSED, false, 1, MODE, false, true>(a);
+        }
+        return heads >= 2048 ? launch_decode<uint16_t, 128, 1, 4, 4, FUSED, false, 1, MODE, true>(a)
+                             : launch_decode<uint16_t, 128, 1, 4, 4, FUSED, false, 1, MODE>(a);
+    }
     if constexpr (MODE != 2) {
         if (a.nsplit == 2) return launch_decode<uint16_t, 128, 2, 4, 8, FUSED, true, 0, MODE>(a);
         if (a.nsplit == 4) return launch_decode<uint16_t, 128, 4, 4, 8, FUSED, true, 0, MODE>(a);
