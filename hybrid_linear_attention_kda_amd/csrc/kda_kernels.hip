@@ -586,7 +586,10 @@ struct NoLoads {
     __device__ __forceinline__ void operator()() const {}
 };
 
-template <class MG, int D, bool ALL = true, class SM = MultiSmem<MG, D>, class After = NoLoads>
+// KEEP: the items also leave the raw inputs of the conv state after T tokens
+// (positions T-3 .. T-1) in sm.cs, so that it is written at the end without
+// loading them again (the chunk form's single chunk).
+template <class MG, int D, bool ALL = true, class SM = MultiSmem<MG, D>, class After = NoLoads, bool KEEP = false>
 __device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, int c0, int n, SM& sm,
                                             After after = After()) {
     typedef typename MG::G G;
@@ -633,6 +636,16 @@ __device__ __forceinline__ void multi_chunk(const Ptrs& p, int T, int m, int h, 
                       conv_silu(u32x2{wb.z, wb.w}, bf16_hi(x0.y), bf16_hi(x1.y), bf16_hi(x2.y), bf16_hi(x3.y))};
             if (g < D / 4) reinterpret_cast<f32x4*>(sm.a[j])[g] = it.av;
             if (g == 0) sm.b[j] = it.bv;
+            if constexpr (KEEP) {
+                // this item's token, and for the first token its older taps
+                // (positions -2 and -1), where they fall in T-3 .. T-1
+                const int tok = c0 + j, sx = tok - (T - 3);
+                if (sx >= 0 && sx < 3) sm.cs[sx][g] = it.xv;
+                if (tok == 0) {
+                    if (T <= 1) sm.cs[1 - T][g] = it.t1;
+                    if (T <= 2) sm.cs[2 - T][g] = it.t2;
+                }
+            }
         }
     };
     if constexpr (ALL) {
@@ -876,6 +889,7 @@ struct WySmem {
     };
     __attribute__((aligned(16))) float G[wy::D];               // P_{n-1}
     float red[4][2][16];                                       // pair sums per wave (64 channels each)
+    u32x2 cs[3][3 * wy::D / 4];                                // bf16 state, one chunk: the new conv state
 };
 
 // The partner lane's value across lane bit B (B = 0, 1: quad swaps; 3: the
@@ -1330,10 +1344,14 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
         };
         // (bf16: the whole state fits beside the chunk's input registers)
         const bool late = sizeof(TS) == 4 && STAG && (blockIdx.x & 1) != 0;
-        multi_chunk<MG, D, true, WySmem>(p, T, m, h, 0, T, sm, [&]() {
+        auto after = [&]() {
             if (!late) half(0);
             if constexpr (sizeof(TS) == 2) half(1);
-        });
+        };
+        // bf16: the new conv state kept in LDS (its reloads at the end would
+        // wait behind the state stores: M = 128 T = 8 141.0 -> 139.1 us,
+        // M = 32 43.5 -> 41.9; f32 1.2% slower with it, so f32 reloads)
+        multi_chunk<MG, D, true, WySmem, decltype(after), sizeof(TS) == 2>(p, T, m, h, 0, T, sm, after);
         if constexpr (sizeof(TS) == 4) {
             if (!late) {
                 half(1);
@@ -1402,9 +1420,16 @@ void decode_wy_kernel(const Ptrs p, const int units, const int T)
 
     if (tid < MG::NGT) {
         const size_t ch = group_channel<typename MG::G, D>(tid, h, 0, HD);
-        const u32x2 n0 = seq_input(p, T, m, C3, ch, T - 3);
-        const u32x2 n1 = seq_input(p, T, m, C3, ch, T - 2);
-        const u32x2 n2 = seq_input(p, T, m, C3, ch, T - 1);
+        u32x2 n0, n1, n2;
+        if constexpr (ONE && sizeof(TS) == 2) {
+            n0 = sm.cs[0][tid];
+            n1 = sm.cs[1][tid];
+            n2 = sm.cs[2][tid];
+        } else {
+            n0 = seq_input(p, T, m, C3, ch, T - 3);
+            n1 = seq_input(p, T, m, C3, ch, T - 2);
+            n2 = seq_input(p, T, m, C3, ch, T - 1);
+        }
         uint16_t* co = p.conv_out + (size_t)m * 3 * C3 + ch;
         st8(co, n0);
         st8(co + C3, n1);
