@@ -104,6 +104,34 @@ def test_store_policy_bitwise_bf16(entry):
     assert torch.equal(S1[:n], S2) and torch.equal(c1[:n], c2) and torch.equal(o1[:n], o2)
 
 
+def test_packed_bf16_equals_unpacked():
+    """bf16 state, plain step: up to 8 heads per CU (2048 on 256 CUs) the
+    kernel keeps the state in its packed registers and unpacks each row
+    twice; above, it holds the rows as f32.  Both form the same products in
+    the same order: 33 streams (2112 heads, the unpacked form) and their
+    first 32 (2048 heads, the packed form) agree bit for bit on those 32."""
+    M, H, D = 33, 64, 128
+    wl = kda_synth.custom("packed", M, H, D, steps=2)
+    li = kda_synth.layer_inputs(wl, 0, DEV, "bf16")
+    res = []
+    for m in (M, M - 1):
+        S = li["state"][:m].clone()
+        cs = li["conv_state"][:m].clone()
+        o = torch.empty((m, H, D), dtype=torch.bfloat16, device=DEV)
+        outs = []
+        for t in range(2):
+            inp = kda_synth.step_inputs(wl, 0, t, DEV)
+            kda_decode_step(S, inp["x"][:m], li["conv_w"], cs, cs, inp["alpha"][:m], inp["beta"][:m],
+                            wl.scale, o)
+            outs.append(o.clone())
+        res.append((S, cs, outs))
+    torch.cuda.synchronize()
+    (S1, c1, o1), (S2, c2, o2) = res
+    n = M - 1
+    assert torch.equal(S1[:n], S2) and torch.equal(c1[:n], c2)
+    assert all(torch.equal(a[:n], b) for a, b in zip(o1, o2))
+
+
 def test_inplace_conv_equals_pingpong():
     wl = kda_synth.custom("pp", 3, 8, 128, steps=4)
     a, oa = run(wl, "f32", 4, nsplit=1, inplace=True)
