@@ -1503,7 +1503,9 @@ static hipError_t launch_decode(const StepArgs& a) {
 //    waves with interleaved rows (fewer heads: idle CUs; more: several
 //    rounds; both slower with bands).
 //  bf16, whole head per workgroup: 4 waves, each owning a band of 32 rows,
-//    16 rows x 4 columns per lane (8-byte accesses), 4 workgroups per CU:
+//    16 rows x 4 columns per lane (8-byte accesses), 4 workgroups per CU
+//    (the plain step in one round of up to 8 heads per CU: the packed form,
+//    8 workgroups per CU, dispatch_wide_bf16):
 //    against 8 waves of 8 rows, M = 8 7.70 / 7.81 us, M = 32 26.1 / 26.7,
 //    M = 128 97.4 / 98.0 (with the hardware bf16 rounding; before it the
 //    8-wave form was the faster one).  With 8 columns per lane and 16-byte
